@@ -1,0 +1,201 @@
+"""CPU oracle for COAT-style FP8 optimizer-state and activation compression.
+
+TEST INFRASTRUCTURE ONLY.  The slow, obviously-correct binary64 reference the
+GPU path is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product package never does.
+
+This module is a thin ctypes wrapper over ``liboracle.so`` (plain C, built by
+``oracle/build.py``).  Every function takes and returns numpy arrays and works
+on the host only.  Arithmetic lives in ``coat_oracle.c``; see its comments for
+the passages of the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+E4M3, E5M2, E2M2 = 0, 1, 2
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m2": E2M2}
+
+_lib = None
+
+
+class HParams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
+    ]
+
+
+def fmt_id(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def lib():
+    """Load (building first if needed) the oracle library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i64, f32, f64, u32, i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint32, ctypes.c_int
+    L.orc_fp8_decode.argtypes, L.orc_fp8_decode.restype = [i32, u32], f64
+    L.orc_fp8_encode.argtypes, L.orc_fp8_encode.restype = [i32, f64], u32
+    L.orc_fp8_max.argtypes, L.orc_fp8_max.restype = [i32], f64
+    L.orc_fp8_min_subnormal.argtypes, L.orc_fp8_min_subnormal.restype = [i32], f64
+    L.orc_fp8_max_code.argtypes, L.orc_fp8_max_code.restype = [i32], u32
+    L.orc_expand_quantize.argtypes = [i32, P, i64, f64, P, P, P]
+    L.orc_expand_quantize.restype = None
+    L.orc_expand_dequantize.argtypes, L.orc_expand_dequantize.restype = [i32, u32, f32, f32], f64
+    L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams)]
+    L.orc_adamw_step.restype = None
+    L.orc_adamw_step_f64.argtypes = [P, P, P, P, i64, ctypes.POINTER(HParams)]
+    L.orc_adamw_step_f64.restype = None
+    L.orc_group_absmax.argtypes = [P, i64, i64, i64, P, P]
+    L.orc_group_absmax.restype = None
+    L.orc_absmax_reduce.argtypes, L.orc_absmax_reduce.restype = [P, i64], f32
+    L.orc_quant_per_tensor.argtypes = [P, i64, f32, P, P]
+    L.orc_quant_per_tensor.restype = None
+    L.orc_quant_group.argtypes = [P, i64, i64, i64, P, P, P]
+    L.orc_quant_group.restype = None
+    _lib = L
+    return L
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def hparams(lr, beta1, beta2, eps, weight_decay, step) -> HParams:
+    return HParams(lr, beta1, beta2, eps, weight_decay, int(step))
+
+
+# ---------------------------------------------------------------- C1 codec
+def decode(fmt, code: int) -> float:
+    return lib().orc_fp8_decode(fmt_id(fmt), int(code))
+
+
+def encode(fmt, x: float) -> int:
+    return int(lib().orc_fp8_encode(fmt_id(fmt), float(x)))
+
+
+def decode_all(fmt, codes) -> np.ndarray:
+    f = fmt_id(fmt)
+    return np.array([lib().orc_fp8_decode(f, int(c)) for c in np.asarray(codes).ravel()])
+
+
+def encode_all(fmt, xs) -> np.ndarray:
+    f = fmt_id(fmt)
+    return np.array([lib().orc_fp8_encode(f, float(x)) for x in np.asarray(xs, dtype=np.float64).ravel()],
+                    dtype=np.uint8 if f != E2M2 else np.uint8)
+
+
+def fmt_max(fmt) -> float:
+    return lib().orc_fp8_max(fmt_id(fmt))
+
+
+def fmt_min_subnormal(fmt) -> float:
+    return lib().orc_fp8_min_subnormal(fmt_id(fmt))
+
+
+def fmt_max_code(fmt) -> int:
+    return int(lib().orc_fp8_max_code(fmt_id(fmt)))
+
+
+# ------------------------------------------------------------- C2/C3 expansion
+def expand_quantize(fmt, x, k_force: float = 0.0):
+    """Quantize one group; returns (codes uint8[G], amax float32, k float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.zeros(x.size, dtype=np.uint8)
+    amax = np.zeros(1, dtype=np.float32)
+    k = np.zeros(1, dtype=np.float32)
+    lib().orc_expand_quantize(fmt_id(fmt), _ptr(x), x.size, float(k_force), _ptr(codes), _ptr(amax), _ptr(k))
+    return codes, np.float32(amax[0]), np.float32(k[0])
+
+
+def expand_dequantize(fmt, codes, amax, k) -> np.ndarray:
+    f = fmt_id(fmt)
+    L = lib()
+    return np.array([L.orc_expand_dequantize(f, int(c), float(amax), float(k))
+                     for c in np.asarray(codes).ravel()])
+
+
+# ------------------------------------------------------------------ C4 AdamW
+def adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, *,
+               G: int, v_fmt, hp: HParams, groups=None, threads: int = 1) -> None:
+    """One FP8-state AdamW step, in place on numpy arrays.
+
+    ``groups`` = (g0, g1) restricts the step to a group range; ``threads``
+    splits that range over host threads (the C code runs without the GIL).
+    """
+    arrs = [param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k]
+    for a in arrs:
+        assert a.flags["C_CONTIGUOUS"]
+    assert param.dtype == np.float32 and grad_bf16.dtype == np.uint16
+    assert m_codes.dtype == np.uint8 and v_codes.dtype == np.uint8
+    n_groups = param.size // G
+    g0, g1 = groups if groups is not None else (0, n_groups)
+    ptrs = [_ptr(a) for a in arrs]
+    L = lib()
+    vf = fmt_id(v_fmt)
+
+    def run(lo, hi):
+        L.orc_adamw_step(*ptrs, lo, hi, G, vf, ctypes.byref(hp))
+
+    if threads <= 1 or g1 - g0 < 2 * threads:
+        run(g0, g1)
+        return
+    bounds = np.linspace(g0, g1, threads + 1).astype(np.int64)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda i: run(int(bounds[i]), int(bounds[i + 1])), range(threads)))
+
+
+def adamw_step_f64(param, grad, m, v, hp: HParams) -> None:
+    for a in (param, grad, m, v):
+        assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    lib().orc_adamw_step_f64(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), param.size, ctypes.byref(hp))
+
+
+# ------------------------------------------------------------ C5 Group Scaling
+def group_absmax(x_bf16, G: int):
+    """Two-stage absmax of a 2-D BF16 (uint16 bits) tensor: (partial, amax)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    partial = np.zeros(rows * (cols // G), dtype=np.float32)
+    amax = np.zeros(1, dtype=np.float32)
+    lib().orc_group_absmax(_ptr(x), rows, cols, G, _ptr(partial), _ptr(amax))
+    return partial, np.float32(amax[0])
+
+
+def absmax_reduce(partial) -> np.float32:
+    p = np.ascontiguousarray(partial, dtype=np.float32)
+    return np.float32(lib().orc_absmax_reduce(_ptr(p), p.size))
+
+
+def quant_per_tensor(x_bf16, amax):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).ravel()
+    codes = np.zeros(x.size, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.float32)
+    lib().orc_quant_per_tensor(_ptr(x), x.size, float(amax), _ptr(codes), _ptr(scale))
+    return codes, np.float32(scale[0])
+
+
+def quant_group(x_bf16, G: int):
+    """1xG E4M3 group quantization: (codes uint8[rows*cols], scales, partial)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros(rows * cols, dtype=np.uint8)
+    scales = np.zeros(rows * (cols // G), dtype=np.float32)
+    partial = np.zeros(rows * (cols // G), dtype=np.float32)
+    lib().orc_quant_group(_ptr(x), rows, cols, G, _ptr(codes), _ptr(scales), _ptr(partial))
+    return codes, scales, partial
