@@ -1,0 +1,141 @@
+"""Python binding of the C ABI in include/coat.h (libcoat.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels.
+Tensors are torch device tensors (torch supplies device memory and streams);
+each function checks dtype, device, size and contiguity, passes raw device
+pointers and the current HIP stream, and raises on a non-zero status.  There
+is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcoat.so")
+
+E4M3, E5M2 = 0, 1
+_FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+
+_lib = None
+
+
+class CoatError(RuntimeError):
+    pass
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
+    ]
+
+
+def lib():
+    """Load libcoat.so (built by activation_compression_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise CoatError(f"{LIB_PATH} is missing: build it with `python activation_compression_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.coat_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i32, ctypes.c_int,
+                                  ctypes.POINTER(AdamWHParams), P]
+    L.coat_group_absmax.argtypes = [P, i64, i64, i32, P, P, P]
+    L.coat_absmax_reduce.argtypes = [P, i64, P, P]
+    L.coat_quant_per_tensor.argtypes = [P, i64, P, P, P, P]
+    L.coat_quant_group.argtypes = [P, i64, i64, i32, P, P, P, P]
+    for f in (L.coat_adamw_step, L.coat_group_absmax, L.coat_absmax_reduce,
+              L.coat_quant_per_tensor, L.coat_quant_group):
+        f.restype = ctypes.c_int
+    L.coat_status_string.argtypes = [ctypes.c_int]
+    L.coat_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().coat_status_string(int(s)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise CoatError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _ptr(t: torch.Tensor | None, dtypes, name: str, numel: int | None = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_U16 = (torch.int16, torch.bfloat16, torch.uint16)
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+
+
+def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step) -> AdamWHParams:
+    return AdamWHParams(lr, beta1, beta2, eps, weight_decay, int(step))
+
+
+def coat_adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, *,
+                    group_size: int = 128, v_format="e4m3", hp: AdamWHParams, n: int | None = None,
+                    stream=None) -> None:
+    """One fused FP8-state AdamW step (see coat_adamw_step in include/coat.h)."""
+    n = param.numel() if n is None else int(n)
+    ng = n // group_size if group_size > 0 else 0
+    args = [_ptr(param, _F32, "param", n), _ptr(grad_bf16, _U16, "grad_bf16", n),
+            _ptr(m_codes, _U8, "m_codes", n), _ptr(m_amax, _F32, "m_amax", ng), _ptr(m_k, _F32, "m_k", ng),
+            _ptr(v_codes, _U8, "v_codes", n), _ptr(v_amax, _F32, "v_amax", ng), _ptr(v_k, _F32, "v_k", ng)]
+    _check(lib().coat_adamw_step(*args, n, group_size, _FMT[v_format], ctypes.byref(hp), _stream(stream)),
+           "coat_adamw_step")
+
+
+def coat_group_absmax(x_bf16, partial_amax, amax, *, group_size: int = 128, stream=None) -> None:
+    """Two-stage Group Scaling absmax of a 2-D BF16 tensor."""
+    rows, cols = x_bf16.shape
+    _check(lib().coat_group_absmax(_ptr(x_bf16, _U16, "x_bf16"), rows, cols, group_size,
+                                   _ptr(partial_amax, _F32, "partial_amax", rows * (cols // group_size)),
+                                   _ptr(amax, _F32, "amax", 1), _stream(stream)), "coat_group_absmax")
+
+
+def coat_absmax_reduce(partial, amax, *, stream=None) -> None:
+    """Stage 2 of Group Scaling alone."""
+    _check(lib().coat_absmax_reduce(_ptr(partial, _F32, "partial"), partial.numel(),
+                                    _ptr(amax, _F32, "amax", 1), _stream(stream)), "coat_absmax_reduce")
+
+
+def coat_quant_per_tensor(x_bf16, amax, codes, scale, *, stream=None) -> None:
+    """Per-tensor E4M3 cast with the device-resident tensor absmax."""
+    n = x_bf16.numel()
+    _check(lib().coat_quant_per_tensor(_ptr(x_bf16, _U16, "x_bf16"), n, _ptr(amax, _F32, "amax", 1),
+                                       _ptr(codes, _U8, "codes", n), _ptr(scale, _F32, "scale", 1),
+                                       _stream(stream)), "coat_quant_per_tensor")
+
+
+def coat_quant_group(x_bf16, codes, scales, partial_amax=None, *, group_size: int = 128, stream=None) -> None:
+    """1xG E4M3 quantization of a 2-D BF16 tensor (optionally also stage 1)."""
+    rows, cols = x_bf16.shape
+    ng = rows * (cols // group_size)
+    _check(lib().coat_quant_group(_ptr(x_bf16, _U16, "x_bf16"), rows, cols, group_size,
+                                  _ptr(codes, _U8, "codes", rows * cols), _ptr(scales, _F32, "scales", ng),
+                                  _ptr(partial_amax, _F32, "partial_amax", ng), _stream(stream)),
+           "coat_quant_group")

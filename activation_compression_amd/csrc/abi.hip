@@ -1,0 +1,134 @@
+// abi.hip -- the C ABI of include/coat.h: argument validation, per-step
+// scalar folding and kernel dispatch.  Nothing is enqueued unless every
+// argument is valid; no device memory is allocated; no call synchronizes.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/coat.h"
+#include "kernels.hpp"
+
+namespace {
+
+using coat::kBlock;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_group(int32_t G) { return G >= 32 && G <= 1024 && (G & (G - 1)) == 0; }
+
+// Workgroups resident at once: CUs x 8, looked up once per device.
+int grid_cap() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int v = cus * 8;
+    if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+coat_status from_hip(hipError_t e) { return e == hipSuccess ? COAT_OK : COAT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *coat_status_string(coat_status s) {
+    switch (s) {
+    case COAT_OK: return "ok";
+    case COAT_ERR_NULL: return "null pointer argument";
+    case COAT_ERR_ALIGN: return "misaligned pointer argument";
+    case COAT_ERR_SHAPE: return "invalid size: n, rows or cols out of range or not a multiple of the group";
+    case COAT_ERR_GROUP: return "group size must be a power of two in [32, 1024]";
+    case COAT_ERR_FORMAT: return "unknown FP8 format";
+    case COAT_ERR_HPARAM: return "invalid AdamW hyper-parameters";
+    case COAT_ERR_HIP: return "HIP runtime error while enqueueing";
+    }
+    return "unknown status";
+}
+
+coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax,
+                            float *m_k, uint8_t *v_codes, float *v_amax, float *v_k, int64_t n,
+                            int32_t group_size, coat_fp8_format v_format, const coat_adamw_hparams *hp,
+                            void *stream) {
+    if (!param || !grad_bf16 || !m_codes || !m_amax || !m_k || !v_codes || !v_amax || !v_k || !hp)
+        return COAT_ERR_NULL;
+    if (!aligned(param, 16) || !aligned(grad_bf16, 16) || !aligned(m_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(m_amax, 4) || !aligned(m_k, 4) || !aligned(v_amax, 4) || !aligned(v_k, 4))
+        return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (n <= 0 || n % group_size != 0) return COAT_ERR_SHAPE;
+    if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
+    if (!isfinite(lr) || !isfinite(wd) || !isfinite(eps) || !(b1 >= 0.0 && b1 < 1.0) ||
+        !(b2 >= 0.0 && b2 < 1.0) || !(eps > 0.0) || hp->step < 1)
+        return COAT_ERR_HPARAM;
+
+    // per-step scalars in binary64, rounded once
+    const double t = (double)hp->step;
+    const double bc1 = 1.0 - pow(b1, t), bc2 = 1.0 - pow(b2, t);
+    coat::StepArgs a;
+    a.param = param; a.grad = grad_bf16;
+    a.m_codes = m_codes; a.m_amax = m_amax; a.m_k = m_k;
+    a.v_codes = v_codes; a.v_amax = v_amax; a.v_k = v_k;
+    a.n = n;
+    a.n_chunks = coat::ceil_div(n, coat::kWaveElems);
+    a.beta1 = hp->beta1; a.omb1 = (float)(1.0 - b1);
+    a.beta2 = hp->beta2; a.omb2 = (float)(1.0 - b2);
+    a.step_size = (float)(lr / bc1);
+    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    a.eps = hp->eps;
+    a.decay = (float)(1.0 - lr * wd);
+    // log2 of each format's range MAX / smallest subnormal
+    a.m_log2_range = (float)(log2(448.0) + 9.0);
+    a.v_log2_range = v_format == COAT_FP8_E5M2 ? (float)(log2(57344.0) + 16.0) : a.m_log2_range;
+    return from_hip(coat::launch_adamw_fp8_step(a, group_size, (int)v_format, (hipStream_t)stream, grid_cap()));
+}
+
+coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t group_size,
+                              float *partial_amax, float *amax, void *stream) {
+    if (!x_bf16 || !partial_amax || !amax) return COAT_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(partial_amax, 4) || !aligned(amax, 4)) return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_group_absmax(x_bf16, rows * cols, group_size, partial_amax, amax,
+                                              (hipStream_t)stream, grid_cap()));
+}
+
+coat_status coat_absmax_reduce(const float *partial, int64_t n, float *amax, void *stream) {
+    if (!partial || !amax) return COAT_ERR_NULL;
+    if (!aligned(partial, 4) || !aligned(amax, 4)) return COAT_ERR_ALIGN;
+    if (n <= 0) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_absmax_reduce(partial, n, amax, (hipStream_t)stream, grid_cap()));
+}
+
+coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float *amax, uint8_t *codes,
+                                  float *scale, void *stream) {
+    if (!x_bf16 || !amax || !codes || !scale) return COAT_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(amax, 4) || !aligned(scale, 4))
+        return COAT_ERR_ALIGN;
+    if (n <= 0 || n % 8 != 0) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_quant_per_tensor(x_bf16, n, amax, codes, scale, (hipStream_t)stream,
+                                                  grid_cap()));
+}
+
+coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t group_size,
+                             uint8_t *codes, float *scales, float *partial_amax_or_null, void *stream) {
+    if (!x_bf16 || !codes || !scales) return COAT_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(scales, 4) ||
+        (partial_amax_or_null && !aligned(partial_amax_or_null, 4)))
+        return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_quant_group(x_bf16, rows * cols, group_size, codes, scales,
+                                             partial_amax_or_null, (hipStream_t)stream, grid_cap()));
+}
+
+}  // extern "C"

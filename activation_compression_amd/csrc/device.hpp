@@ -1,0 +1,111 @@
+// device.hpp -- gfx950 device primitives shared by the COAT kernels:
+// format traits, native OCP FP8 conversions, wave64 group reductions and
+// small exact-arithmetic helpers.  Header-only, device code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coat {
+
+enum Fmt : int { kE4M3 = 0, kE5M2 = 1 };
+
+// OCP FP8 formats ("LLM atlas -- systems / numerics", sections "01 Number
+// anatomy" and "03 FP8"): E4M3 max 448, smallest subnormal 2^-9;
+// E5M2 max 57344, smallest subnormal 2^-16.
+template <int F> struct Fp8;
+template <> struct Fp8<kE4M3> {
+    static constexpr float kMax = 448.0f;
+    static constexpr double kMinSub = 0x1p-9;
+};
+template <> struct Fp8<kE5M2> {
+    static constexpr float kMax = 57344.0f;
+    static constexpr double kMinSub = 0x1p-16;
+};
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// ---- native FP8 conversions (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 and the
+// reverse).  Rounding is to nearest even; callers clamp to +-MAX first, which
+// makes the result the saturating rounding whatever the overflow mode.
+
+// Pack four FP32 values into four FP8 codes (byte i <- value i).
+template <int F>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    int w;
+    if constexpr (F == kE4M3) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    }
+    return (uint32_t)w;
+}
+
+// Decode code byte 0 of `c` to FP32.
+template <int F>
+__device__ __forceinline__ float decode1(uint32_t c) {
+    if constexpr (F == kE4M3)
+        return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+    else
+        return __builtin_amdgcn_cvt_f32_bf8((int)c, 0);
+}
+
+// ---- bit helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Magnitude of `mag` with the sign bit of `sgn` (one v_bfi_b32).
+__device__ __forceinline__ float with_sign_of(float mag, float sgn) {
+    return __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (__float_as_uint(sgn) & 0x80000000u));
+}
+
+// ---- wave64 reductions over aligned runs of W lanes (W a power of two <= 64).
+// Every lane of a run receives the run's result.  Runs of up to 16 lanes stay
+// inside a DPP row; 32 uses ds_swizzle, 64 ds_bpermute.
+
+template <int W>
+__device__ __forceinline__ uint32_t run_max(uint32_t v) {
+    if constexpr (W >= 2) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    if constexpr (W >= 4) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    if constexpr (W >= 8) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    if constexpr (W >= 16) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true)); // row_mirror
+    if constexpr (W >= 32) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));             // xor 16
+    if constexpr (W >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t run_min(uint32_t v) {
+    if constexpr (W >= 2) v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    if constexpr (W >= 4) v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+    if constexpr (W >= 8) v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));
+    if constexpr (W >= 16) v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));
+    if constexpr (W >= 32) v = min(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    if constexpr (W >= 64) v = min(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
+// Max of the packed |bf16| magnitudes of one dword pair-wise (v_pk_max_u16
+// on the bit patterns with the sign bits cleared: for non-negative IEEE
+// values the integer order is the numeric order, denormals included).
+__device__ __forceinline__ uint32_t pk_absmax_u16(uint32_t acc, uint32_t w) {
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    uint32_t a = w & 0x7FFF7FFFu;
+    v2u16 x = __builtin_bit_cast(v2u16, acc), y = __builtin_bit_cast(v2u16, a);
+    v2u16 r = __builtin_elementwise_max(x, y);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Correctly rounded quotient a / b from the correctly rounded reciprocal
+// y = RN(1/b): one product and one FMA-based correction (Markstein's
+// theorem; no overflow or underflow in the operands' range).
+__device__ __forceinline__ float div_rn_from_rcp(float a, float b, float y) {
+    float q = a * y;
+    float r = __builtin_fmaf(-q, b, a);
+    return __builtin_fmaf(r, y, q);
+}
+
+}  // namespace coat

@@ -1,0 +1,245 @@
+// group_scaling.hip -- COAT Group Scaling and activation FP8 casts for gfx950.
+//
+// Method: "COAT: compressing optimizer states and activations for
+// memory-efficient FP8 training" explainer (blog.daoxuan.cc/posts/57954),
+// section "mixed granularity": linear-layer inputs take one per-tensor E4M3
+// scale, whose absmax is found in two stages (a max per 1xG slice, cached,
+// then a max over that G-times-smaller tensor); nonlinear-layer inputs take
+// one scale per 1xG slice along the channel axis.
+//
+// All kernels are HBM-streaming: each lane owns 16 consecutive BF16 values
+// (two 16-byte loads) and writes 16 codes with one 16-byte store.  |x| maxima
+// are integer maxima of the BF16 bit patterns with the sign cleared (two per
+// v_pk_max_u16), which is exact for every finite value, denormals included.
+// A 1xG slice is G/16 adjacent lanes, reduced with DPP.
+//
+// Every cast evaluates y = FP32(448 x / a) exactly rounded: a is prescaled by
+// a power of two into [1, 2) (exact), 448 x by the same power (exact: a BF16
+// value times 7 * 2^j has at most 11 significant bits), and the quotient is
+// the RN-reciprocal product plus one Markstein correction.  The code is then
+// the round-to-nearest-even of y, clamped to +-448.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace coat {
+namespace {
+
+// Abs-max bits (low 16 = BF16 pattern) of 16 BF16 values held in 8 dwords.
+__device__ __forceinline__ uint32_t absmax16(const uint32_t w[8]) {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = pk_absmax_u16(acc, w[i]);
+    return max(acc & 0xFFFFu, acc >> 16);
+}
+
+__device__ __forceinline__ void load16(const uint16_t *p, uint32_t w[8]) {
+    const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
+    const uint4 b = reinterpret_cast<const uint4 *>(p)[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// Scaling constants for a (non-negative) absmax a: a = a_s 2^-sh, a_s in [1, 2).
+struct CastQ {
+    float mult;   // 448 * 2^sh: x * mult is exact
+    float a_s;    // prescaled absmax
+    float inv_s;  // RN(1 / a_s)
+};
+
+__device__ __forceinline__ CastQ cast_q(float a) {
+    CastQ q;
+    if (!(a > 0.0f)) {  // all-zero tensor / slice: every code 0
+        q.mult = 0.0f; q.a_s = 1.0f; q.inv_s = 1.0f;
+        return q;
+    }
+    int e;
+    const float ma = frexpf(a, &e);
+    q.a_s = 2.0f * ma;
+    q.mult = __builtin_amdgcn_ldexpf(448.0f, 1 - e);
+    q.inv_s = 1.0f / q.a_s;
+    return q;
+}
+
+// E4M3 codes of 16 BF16 values.
+__device__ __forceinline__ uint4 cast16(const uint32_t w[8], const CastQ &q) {
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float x = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+        const float t = div_rn_from_rcp(x * q.mult, q.a_s, q.inv_s);
+        y[i] = __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+    }
+    return make_uint4(cvt4<kE4M3>(y[0], y[1], y[2], y[3]), cvt4<kE4M3>(y[4], y[5], y[6], y[7]),
+                      cvt4<kE4M3>(y[8], y[9], y[10], y[11]), cvt4<kE4M3>(y[12], y[13], y[14], y[15]));
+}
+
+// ---- stage 1: per-slice absmax; also clears the stage-2 target, which the
+// stage-2 kernel (next on the same stream) max-reduces into.
+template <int G>
+__global__ __launch_bounds__(kBlock) void absmax_stage1_kernel(const uint16_t *__restrict__ x, int64_t n,
+                                                               int64_t n_chunks, float *__restrict__ partial,
+                                                               float *__restrict__ amax) {
+    constexpr int LPG = G / 16;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *amax = 0.0f;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
+    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+        const int64_t e0 = chunk * kWaveElems + lane * 16;
+        const bool act = e0 < n;
+        uint32_t m = 0u;
+        if (act) {
+            uint32_t w[8];
+            load16(x + e0, w);
+            m = absmax16(w);
+        }
+        m = run_max<LPG>(m);
+        if (act && (lane % LPG) == 0) partial[e0 / G] = __uint_as_float(m << 16);
+    }
+}
+
+// ---- stage 2: max over the partial tensor.  Multi-workgroup; each
+// workgroup folds its maximum into *amax with an atomic max on the bit
+// pattern (order-independent and exact for non-negative floats).
+__global__ __launch_bounds__(kBlock) void absmax_stage2_kernel(const float *__restrict__ partial, int64_t n,
+                                                               float *__restrict__ amax) {
+    __shared__ uint32_t red[kBlock / 64];
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        m = max(m, __float_as_uint(partial[i]) & 0x7FFFFFFFu);
+    m = run_max<64>(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = red[0];
+#pragma unroll
+        for (int i = 1; i < kBlock / 64; ++i) b = max(b, red[i]);
+        if (b != 0u) atomicMax(reinterpret_cast<unsigned int *>(amax), b);
+    }
+}
+
+__global__ void zero_scalar_kernel(float *p) { *p = 0.0f; }
+
+// ---- per-tensor cast with the device-resident tensor absmax.
+__global__ __launch_bounds__(kBlock) void quant_per_tensor_kernel(const uint16_t *__restrict__ x, int64_t n,
+                                                                  int64_t n_chunks, const float *__restrict__ amax,
+                                                                  uint8_t *__restrict__ codes,
+                                                                  float *__restrict__ scale) {
+    const float A = *amax;
+    const CastQ q = cast_q(A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = A > 0.0f ? A / 448.0f : 1.0f;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
+    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+        const int64_t e0 = chunk * kWaveElems + lane * 16;
+        if (e0 + 16 <= n) {
+            uint32_t w[8];
+            load16(x + e0, w);
+            *reinterpret_cast<uint4 *>(codes + e0) = cast16(w, q);
+        } else if (e0 < n) {  // n % 16 == 8: the last lane holds 8 values
+            uint32_t w[8];
+            const uint4 a = reinterpret_cast<const uint4 *>(x + e0)[0];
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = w[5] = w[6] = w[7] = 0u;
+            const uint4 c = cast16(w, q);
+            *reinterpret_cast<uint2 *>(codes + e0) = make_uint2(c.x, c.y);
+        }
+    }
+}
+
+// ---- 1xG group cast (+ optional stage-1 partials from the same pass).
+template <int G>
+__global__ __launch_bounds__(kBlock) void quant_group_kernel(const uint16_t *__restrict__ x, int64_t n,
+                                                             int64_t n_chunks, uint8_t *__restrict__ codes,
+                                                             float *__restrict__ scales,
+                                                             float *__restrict__ partial) {
+    constexpr int LPG = G / 16;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
+    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+        const int64_t e0 = chunk * kWaveElems + lane * 16;
+        const bool act = e0 < n;
+        uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if (act) load16(x + e0, w);
+        const uint32_t mb = run_max<LPG>(absmax16(w));
+        const float a = __uint_as_float(mb << 16);
+        const CastQ q = cast_q(a);
+        const uint4 c = cast16(w, q);
+        if (act) {
+            *reinterpret_cast<uint4 *>(codes + e0) = c;
+            if ((lane % LPG) == 0) {
+                const int64_t grp = e0 / G;
+                scales[grp] = a > 0.0f ? a / 448.0f : 1.0f;
+                if (partial) partial[grp] = a;
+            }
+        }
+    }
+}
+
+dim3 grid_for(int64_t n_chunks, int grid_cap) {
+    const int64_t blocks = ceil_div(n_chunks, kBlock / 64);
+    return dim3((unsigned)(blocks < grid_cap ? blocks : grid_cap));
+}
+
+template <typename K, typename... Args>
+hipError_t launch_k(K kernel, dim3 grid, hipStream_t s, Args... args) {
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), ptrs, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_absmax_reduce(const float *partial, int64_t n, float *amax, hipStream_t s, int grid_cap) {
+    hipError_t e = launch_k(&zero_scalar_kernel, dim3(1), s, amax);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = ceil_div(n, (int64_t)kBlock * 4);
+    const dim3 grid((unsigned)(blocks < grid_cap ? (blocks > 0 ? blocks : 1) : grid_cap));
+    return launch_k(&absmax_stage2_kernel, grid, s, partial, n, amax);
+}
+
+hipError_t launch_group_absmax(const uint16_t *x, int64_t n, int G, float *partial, float *amax,
+                               hipStream_t s, int grid_cap) {
+    const int64_t nc = ceil_div(n, kWaveElems);
+    const dim3 grid = grid_for(nc, grid_cap);
+    hipError_t e;
+    switch (G) {
+    case 32: e = launch_k(&absmax_stage1_kernel<32>, grid, s, x, n, nc, partial, amax); break;
+    case 64: e = launch_k(&absmax_stage1_kernel<64>, grid, s, x, n, nc, partial, amax); break;
+    case 128: e = launch_k(&absmax_stage1_kernel<128>, grid, s, x, n, nc, partial, amax); break;
+    case 256: e = launch_k(&absmax_stage1_kernel<256>, grid, s, x, n, nc, partial, amax); break;
+    case 512: e = launch_k(&absmax_stage1_kernel<512>, grid, s, x, n, nc, partial, amax); break;
+    case 1024: e = launch_k(&absmax_stage1_kernel<1024>, grid, s, x, n, nc, partial, amax); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t np = n / G;
+    const int64_t blocks = ceil_div(np, (int64_t)kBlock * 4);
+    const dim3 g2((unsigned)(blocks < grid_cap ? (blocks > 0 ? blocks : 1) : grid_cap));
+    return launch_k(&absmax_stage2_kernel, g2, s, (const float *)partial, np, amax);
+}
+
+hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *amax, uint8_t *codes,
+                                   float *scale, hipStream_t s, int grid_cap) {
+    const int64_t nc = ceil_div(n, kWaveElems);
+    return launch_k(&quant_per_tensor_kernel, grid_for(nc, grid_cap), s, x, n, nc, amax, codes, scale);
+}
+
+hipError_t launch_quant_group(const uint16_t *x, int64_t n, int G, uint8_t *codes, float *scales,
+                              float *partial, hipStream_t s, int grid_cap) {
+    const int64_t nc = ceil_div(n, kWaveElems);
+    const dim3 grid = grid_for(nc, grid_cap);
+    switch (G) {
+    case 32: return launch_k(&quant_group_kernel<32>, grid, s, x, n, nc, codes, scales, partial);
+    case 64: return launch_k(&quant_group_kernel<64>, grid, s, x, n, nc, codes, scales, partial);
+    case 128: return launch_k(&quant_group_kernel<128>, grid, s, x, n, nc, codes, scales, partial);
+    case 256: return launch_k(&quant_group_kernel<256>, grid, s, x, n, nc, codes, scales, partial);
+    case 512: return launch_k(&quant_group_kernel<512>, grid, s, x, n, nc, codes, scales, partial);
+    case 1024: return launch_k(&quant_group_kernel<1024>, grid, s, x, n, nc, codes, scales, partial);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace coat

@@ -1,0 +1,48 @@
+// kernels.hpp -- internal launch interface between the C ABI (abi.hip) and
+// the kernel translation units.  Host code; no torch, no oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coat {
+
+// Arguments of the fused FP8-state AdamW step, with the per-step scalars
+// already folded on the host (binary64, rounded once to FP32).
+struct StepArgs {
+    float *param;
+    const uint16_t *grad;
+    uint8_t *m_codes;
+    float *m_amax, *m_k;
+    uint8_t *v_codes;
+    float *v_amax, *v_k;
+    int64_t n;            // parameters
+    int64_t n_chunks;     // ceil(n / 1024): one wave handles 1024 per pass
+    float beta1, omb1;    // beta1 and 1 - beta1 (exact in FP32 for beta1 in [0.5, 1))
+    float beta2, omb2;
+    float step_size;      // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
+    float eps;
+    float decay;          // 1 - lr * weight_decay
+    float m_log2_range;   // log2(MAX / smallest subnormal) of m's format
+    float v_log2_range;   // ... of v's format
+};
+
+hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
+                                 hipStream_t stream, int grid_cap);
+
+hipError_t launch_group_absmax(const uint16_t *x, int64_t n, int group_size, float *partial,
+                               float *amax, hipStream_t stream, int grid_cap);
+hipError_t launch_absmax_reduce(const float *partial, int64_t n, float *amax,
+                                hipStream_t stream, int grid_cap);
+hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *amax,
+                                   uint8_t *codes, float *scale, hipStream_t stream, int grid_cap);
+hipError_t launch_quant_group(const uint16_t *x, int64_t n, int group_size, uint8_t *codes,
+                              float *scales, float *partial, hipStream_t stream, int grid_cap);
+
+constexpr int kBlock = 256;       // threads per workgroup: 4 wave64s
+constexpr int kWaveElems = 1024;  // elements per wave pass: 64 lanes x 16
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace coat

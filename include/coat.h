@@ -1,0 +1,173 @@
+/*
+ * coat.h -- C ABI of the MI355X (gfx950) kernels for COAT-style FP8
+ * compression of AdamW optimizer states and activations.
+ *
+ * Sources (the pages the method is described on):
+ *   [COAT]  "COAT: compressing optimizer states and activations for
+ *           memory-efficient FP8 training" explainer, blog.daoxuan.cc/posts/57954
+ *   [ATLAS] "LLM atlas -- systems / numerics", llm-atlas.k1412.top/systems/numerics
+ *   [LPF]   "AI low-precision formats (bfloat16/FP8/TF32)" interview notes,
+ *           codechuan.com/interview/1/948.html
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *   allocates no device memory, keeps no state between calls and never
+ *   synchronizes: all work is enqueued on `stream` (a hipStream_t passed as
+ *   void*, NULL for the default stream) and every result, including
+ *   per-tensor statistics, is written to device memory.
+ * - Arguments are validated before anything is enqueued.  On any error the
+ *   call returns a non-zero coat_status, enqueues nothing and leaves every
+ *   buffer untouched.  Launch failures return COAT_ERR_HIP.  Device faults
+ *   surface at the caller's next synchronization of `stream`.
+ * - Distinct arrays must not overlap.  Calls on disjoint buffers may run
+ *   concurrently from any host thread.  No C++ exception crosses the ABI.
+ * - BF16 values are passed as their 16-bit patterns (uint16_t); FP8 codes as
+ *   uint8_t in the OCP encodings: E4M3 (bias 7, max 448, smallest subnormal
+ *   2^-9, only S.1111.111 is NaN) and E5M2 (bias 15, max 57344, smallest
+ *   subnormal 2^-16) -- [ATLAS] sections "01 Number anatomy" and "03 FP8".
+ *   Codes 0x00 and 0x80 both mean zero.  No NaN or infinity code is produced.
+ * - FP8 rounding is round-to-nearest-even with saturation at +-MAX.
+ * - Group size G: a power of two in [32, 1024].  Groups are 1xG runs of
+ *   contiguous elements ([COAT] section "mixed granularity": along the channel
+ *   axis, never across tokens); the optimizer groups are consecutive runs of
+ *   the flat parameter arena, so a tensor whose size is a multiple of G never
+ *   shares a group with its neighbour.
+ * - NaN or infinite inputs are outside the contract.
+ */
+#ifndef COAT_H
+#define COAT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    COAT_OK = 0,
+    COAT_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    COAT_ERR_ALIGN = 2,  /* a pointer misses its required alignment             */
+    COAT_ERR_SHAPE = 3,  /* n / rows / cols out of range or not divisible       */
+    COAT_ERR_GROUP = 4,  /* group size not a power of two in [32, 1024]         */
+    COAT_ERR_FORMAT = 5, /* unknown FP8 format                                  */
+    COAT_ERR_HPARAM = 6, /* beta outside [0,1), eps <= 0, step < 1, non-finite  */
+    COAT_ERR_HIP = 7     /* the HIP runtime refused the launch                  */
+} coat_status;
+
+typedef enum {
+    COAT_FP8_E4M3 = 0,
+    COAT_FP8_E5M2 = 1
+} coat_fp8_format;
+
+/* AdamW hyper-parameters, FP32 as the caller holds them.  `step` is the
+ * 1-based index of the update being made (the caller increments it before
+ * each call); it drives the bias corrections 1 - beta^step. */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} coat_adamw_hparams;
+
+/*
+ * coat_adamw_step -- one fused AdamW update of n parameters whose moments are
+ * stored in FP8 with per-group dynamic-range expansion.
+ *
+ * Per 1xG group and per step ([COAT] sections on second-moment sensitivity,
+ * on the smaller dynamic range of v, and "expansion function"; the update rule
+ * of [ATLAS] section "08 Adam -> AdamW"; FP32 master weights per [LPF]):
+ *   1. dequantize m and v:  x = sign(c) * amax * (|dec(c)| / MAX)^(1/k)
+ *      with the group's stored (amax, k) -- the inverse of f(x) = sign(x)|x|^k;
+ *   2. AdamW in FP32 on the FP32 master weights:
+ *        m' = b1 m + (1-b1) g,   v' = b2 v + (1-b2) g^2,
+ *        theta' = (1 - lr wd) theta - lr (m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps);
+ *   3. per group, amax = max|x| and amin = min over nonzero |x| of the new
+ *      moment, k = ln(MAX / min_subnormal) / ln(amax / amin) so that the
+ *      expanded group fills the FP8 range (k = 1 when amax = amin or amax = 0;
+ *      k < 1 is allowed for groups wider than the format);
+ *   4. requantize: c = RNE_sat(sign(x) * MAX * (|x| / amax)^k); store the codes
+ *      and the new (amax, k).
+ *
+ * param      FP32 [n], read and written.                  16-byte aligned.
+ * grad_bf16  BF16 bit patterns [n], read only.            16-byte aligned.
+ * m_codes    E4M3 codes [n], read and written.            16-byte aligned.
+ * m_amax     FP32 [n/G] group absmax of m, read/written.  4-byte aligned.
+ * m_k        FP32 [n/G] expansion exponent of m.          4-byte aligned.
+ * v_codes    codes [n] in `v_format`, read and written.   16-byte aligned.
+ * v_amax, v_k  as for m.
+ * n          number of parameters, > 0, a multiple of G.  A parameter set is
+ *            passed as one flat arena (one launch for the whole model).
+ * group_size G.   v_format  COAT_FP8_E4M3 or COAT_FP8_E5M2 (m is always E4M3).
+ * hp         host pointer, read during the call only.
+ * A never-updated state is codes 0, amax 0, k 1.
+ */
+coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16,
+                            uint8_t *m_codes, float *m_amax, float *m_k,
+                            uint8_t *v_codes, float *v_amax, float *v_k,
+                            int64_t n, int32_t group_size, coat_fp8_format v_format,
+                            const coat_adamw_hparams *hp, void *stream);
+
+/*
+ * coat_group_absmax -- both stages of Group Scaling ([COAT] section "mixed
+ * granularity"): stage 1 writes the max |x| of every 1xG slice of each row,
+ * stage 2 reduces that G-times-smaller tensor to the tensor absmax.
+ *
+ * x_bf16        BF16 [rows x cols] row-major, read only.  16-byte aligned.
+ * rows, cols    rows > 0; cols > 0, a multiple of G.
+ * partial_amax  FP32 [rows * cols / G], written (row r, slice j at r*(cols/G)+j).
+ *               4-byte aligned.
+ * amax          FP32 [1], written: max over partial_amax (exact; both are
+ *               BF16 values held in FP32).
+ */
+coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                              int32_t group_size, float *partial_amax, float *amax,
+                              void *stream);
+
+/*
+ * coat_absmax_reduce -- stage 2 of Group Scaling alone, for partial maxima
+ * produced elsewhere (for example by coat_quant_group): amax = max partial.
+ *
+ * partial  FP32 [n] non-negative values, read only.  4-byte aligned.  n > 0.
+ * amax     FP32 [1], written.
+ */
+coat_status coat_absmax_reduce(const float *partial, int64_t n, float *amax, void *stream);
+
+/*
+ * coat_quant_per_tensor -- per-tensor E4M3 cast of a linear-layer input with
+ * current (just-in-time) scaling from the tensor's own absmax ([COAT] section
+ * "mixed granularity"):
+ *   A = *amax (device scalar, e.g. from coat_group_absmax, read on device);
+ *   code = RNE_sat(y) with y the FP32 value of 448 * x / A (correctly
+ *   rounded quotient); *scale = FP32(A / 448), the dequantization scale.
+ *   A = 0 gives scale 1 and all codes 0.
+ *
+ * x_bf16  BF16 [n], read only.  16-byte aligned.  n > 0, a multiple of 8.
+ * amax    FP32 [1] device scalar, read only.
+ * codes   E4M3 [n], written.  16-byte aligned.
+ * scale   FP32 [1], written.
+ */
+coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float *amax,
+                                  uint8_t *codes, float *scale, void *stream);
+
+/*
+ * coat_quant_group -- 1xG E4M3 quantization of a nonlinear-layer input
+ * ([COAT] section "mixed granularity"): per slice a = max |x|,
+ * code = RNE_sat(FP32(448 * x / a)), scale = FP32(a / 448); a = 0 gives
+ * scale 1 and codes 0.  When partial_amax_or_null is not NULL it also
+ * receives a -- stage 1 of Group Scaling from the same pass.
+ *
+ * x_bf16   BF16 [rows x cols] row-major, read only.  16-byte aligned.
+ * codes    E4M3 [rows x cols], written.  16-byte aligned.
+ * scales   FP32 [rows * cols / G], written.  4-byte aligned.
+ * partial_amax_or_null  FP32 [rows * cols / G] or NULL.
+ */
+coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                             int32_t group_size, uint8_t *codes, float *scales,
+                             float *partial_amax_or_null, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *coat_status_string(coat_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COAT_H */

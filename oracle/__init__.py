@@ -167,14 +167,36 @@ def adamw_step_f64(param, grad, m, v, hp: HParams) -> None:
 
 
 # ------------------------------------------------------------ C5 Group Scaling
-def group_absmax(x_bf16, G: int):
-    """Two-stage absmax of a 2-D BF16 (uint16 bits) tensor: (partial, amax)."""
+def _row_blocks(rows: int, threads: int):
+    t = max(1, min(threads, rows))
+    b = np.linspace(0, rows, t + 1).astype(np.int64)
+    return [(int(b[i]), int(b[i + 1])) for i in range(t) if b[i + 1] > b[i]]
+
+
+def _run_blocks(fn, blocks, threads):
+    if len(blocks) == 1 or threads <= 1:
+        for lo, hi in blocks:
+            fn(lo, hi)
+        return
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda b: fn(*b), blocks))
+
+
+def group_absmax(x_bf16, G: int, threads: int = 1):
+    """Two-stage absmax of a 2-D BF16 (uint16 bits) tensor: (partial, amax).
+    ``threads`` splits stage 1 by rows; stage 2 runs once over all partials."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     rows, cols = x.shape
-    partial = np.zeros(rows * (cols // G), dtype=np.float32)
-    amax = np.zeros(1, dtype=np.float32)
-    lib().orc_group_absmax(_ptr(x), rows, cols, G, _ptr(partial), _ptr(amax))
-    return partial, np.float32(amax[0])
+    gpr = cols // G
+    partial = np.zeros(rows * gpr, dtype=np.float32)
+    L = lib()
+
+    def run(lo, hi):
+        tmp = np.zeros(1, dtype=np.float32)
+        L.orc_group_absmax(_ptr(x[lo:hi]), hi - lo, cols, G, _ptr(partial[lo * gpr:hi * gpr]), _ptr(tmp))
+
+    _run_blocks(run, _row_blocks(rows, threads), threads)
+    return partial, absmax_reduce(partial)
 
 
 def absmax_reduce(partial) -> np.float32:
@@ -182,20 +204,34 @@ def absmax_reduce(partial) -> np.float32:
     return np.float32(lib().orc_absmax_reduce(_ptr(p), p.size))
 
 
-def quant_per_tensor(x_bf16, amax):
-    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).ravel()
+def quant_per_tensor(x_bf16, amax, threads: int = 1):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1)
     codes = np.zeros(x.size, dtype=np.uint8)
     scale = np.zeros(1, dtype=np.float32)
-    lib().orc_quant_per_tensor(_ptr(x), x.size, float(amax), _ptr(codes), _ptr(scale))
+    L = lib()
+    n = x.size
+    bounds = [(lo * 16, min(n, hi * 16)) for lo, hi in _row_blocks((n + 15) // 16, threads)]
+
+    def run(lo, hi):
+        L.orc_quant_per_tensor(_ptr(x[lo:hi]), hi - lo, float(amax), _ptr(codes[lo:hi]), _ptr(scale))
+
+    _run_blocks(run, bounds, threads)
     return codes, np.float32(scale[0])
 
 
-def quant_group(x_bf16, G: int):
+def quant_group(x_bf16, G: int, threads: int = 1):
     """1xG E4M3 group quantization: (codes uint8[rows*cols], scales, partial)."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     rows, cols = x.shape
+    gpr = cols // G
     codes = np.zeros(rows * cols, dtype=np.uint8)
-    scales = np.zeros(rows * (cols // G), dtype=np.float32)
-    partial = np.zeros(rows * (cols // G), dtype=np.float32)
-    lib().orc_quant_group(_ptr(x), rows, cols, G, _ptr(codes), _ptr(scales), _ptr(partial))
+    scales = np.zeros(rows * gpr, dtype=np.float32)
+    partial = np.zeros(rows * gpr, dtype=np.float32)
+    L = lib()
+
+    def run(lo, hi):
+        L.orc_quant_group(_ptr(x[lo:hi]), hi - lo, cols, G, _ptr(codes[lo * cols:hi * cols]),
+                          _ptr(scales[lo * gpr:hi * gpr]), _ptr(partial[lo * gpr:hi * gpr]))
+
+    _run_blocks(run, _row_blocks(rows, threads), threads)
     return codes, scales, partial

@@ -1,0 +1,152 @@
+"""Helpers shared by the GPU parity tests: run one step on each side from the
+same inputs and compare to the stated tolerances.
+
+Tolerances (the product's contract with the oracle):
+* theta (FP32 master weights): |gpu - ref| <= 1e-6 |ref| + 1e-6 lr.  The
+  absolute floor covers parameters that land near zero, where a relative
+  bound is undefined; 1e-6 lr is a millionth of a typical update.
+* FP8 codes: identical (0x00 == 0x80) on >= 99.99% of each moment tensor and
+  every mismatch exactly one grid step -- the GPU evaluates the power with
+  FP32 exp2/log2 while the oracle uses binary64 pow, so an element within an
+  ulp or so of a rounding midpoint may land on the neighbouring code.
+* amax: within the FP32 rounding bound of the moment update, 2^-21 (2 amax_prev
+  + amax) (a few ulps: the dequantized old moment carries the exp2 rounding).
+* k: within 1e-5 relative, plus the first-order effect on k of the FP32
+  rounding bound of the group's smallest moment (dk/k = (d amin/amin) /
+  ln(amax/amin)).  The smallest moment of a group is often a near-cancellation
+  b1 m + (1-b1) g, whose FP32 value carries an absolute error of a few ulps of
+  the terms, i.e. of max(amax_prev, amax); that error is bounded here by
+  2^-21 (2 amax_prev + amax).  Groups whose range is below 1.01 or whose
+  smallest moment is within that bound of zero are judged by their codes only.
+* Activation path: partial maxima, amax, scales and codes bit-exact.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as orc
+from activation_compression_amd import coat, inputs
+
+LR, B1, B2, EPS, WD = (float(np.float32(v)) for v in
+                       (inputs.LR, inputs.BETA1, inputs.BETA2, inputs.EPS, inputs.WEIGHT_DECAY))
+THREADS = 8
+CODE_MATCH_MIN = 0.9999
+
+
+def flush(msg: str):
+    print(msg, flush=True)
+
+
+def gpu_hp(step):
+    return coat.adamw_hparams(LR, B1, B2, EPS, WD, step)
+
+
+def orc_hp(step):
+    return orc.hparams(LR, B1, B2, EPS, WD, step)
+
+
+def np_state(n, G):
+    return {k: v.numpy() for k, v in inputs.fresh_state(n, G).items()}
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def gpu_step(theta, g_bits, st, G, v_fmt, t):
+    """One coat_adamw_step on copies of the given host arrays; returns host copies."""
+    th = dev(theta)
+    s = {k: dev(v) for k, v in st.items()}
+    coat.coat_adamw_step(th, dev(g_bits), s["m_codes"], s["m_amax"], s["m_k"], s["v_codes"],
+                         s["v_amax"], s["v_k"], group_size=G, v_format=v_fmt, hp=gpu_hp(t))
+    torch.cuda.synchronize()
+    return host(th), {k: host(v) for k, v in s.items()}
+
+
+def oracle_step(theta, g_bits, st, G, v_fmt, t, threads=THREADS):
+    th = theta.copy()
+    s = {k: v.copy() for k, v in st.items()}
+    orc.adamw_step(th, g_bits, s["m_codes"], s["m_amax"], s["m_k"], s["v_codes"], s["v_amax"], s["v_k"],
+                   G=G, v_fmt=v_fmt, hp=orc_hp(t), threads=threads)
+    return th, s
+
+
+def code_diff(gpu: np.ndarray, ref: np.ndarray):
+    """(fraction identical, max grid-step distance) with 0x00 == 0x80."""
+    g = gpu.astype(np.int32)
+    r = ref.astype(np.int32)
+    g = np.where((g & 0x7F) == 0, 0, g)
+    r = np.where((r & 0x7F) == 0, 0, r)
+    same = g == r
+    frac = float(same.mean()) if same.size else 1.0
+    if same.all():
+        return frac, 0
+    sg = np.where(g & 0x80, -1, 1) * (g & 0x7F)
+    sr = np.where(r & 0x80, -1, 1) * (r & 0x7F)
+    return frac, int(np.abs(sg - sr).max())
+
+
+def assert_codes(gpu, ref, what, min_frac=CODE_MATCH_MIN):
+    frac, steps = code_diff(gpu, ref)
+    assert frac >= min_frac, f"{what}: only {frac:.6%} codes identical"
+    assert steps <= 1, f"{what}: a code differs by {steps} grid steps"
+    return frac
+
+
+def assert_theta(gpu, ref, what):
+    ref64 = ref.astype(np.float64)
+    err = np.abs(gpu.astype(np.float64) - ref64)
+    tol = 1e-6 * np.abs(ref64) + 1e-6 * LR
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} params out of tolerance; worst "
+                           f"err {err[bad].max():.3e} at |ref| {np.abs(ref64[bad][np.argmax(err[bad])]):.3e}")
+
+
+def assert_amax(gpu, ref, amax_prev, what):
+    ref = ref.astype(np.float64)
+    tol = np.maximum(2.0 ** -21 * (2 * np.abs(amax_prev.astype(np.float64)) + ref),
+                     np.spacing(np.abs(ref).astype(np.float32)))
+    d = np.abs(gpu.astype(np.float64) - ref)
+    bad = d > tol
+    assert not bad.any(), f"{what}: amax off in {int(bad.sum())} groups (worst {(d / np.maximum(ref, 1e-45)).max():.3e} rel)"
+
+
+def assert_k(gpu, ref, amax_ref, amax_prev, v_fmt_name, what):
+    r_fmt = orc.fmt_max(v_fmt_name) / orc.fmt_min_subnormal(v_fmt_name)
+    ref = ref.astype(np.float64)
+    amax = amax_ref.astype(np.float64)
+    ln_ratio = math.log(r_fmt) / ref                 # ln(amax / amin) from the stored k
+    amin = amax * np.exp(-ln_ratio)
+    delta = 2.0 ** -21 * (2 * np.abs(amax_prev.astype(np.float64)) + amax)
+    well = (ln_ratio >= math.log(1.01)) & (delta < 0.5 * amin) & (amax > 0)
+    tol = 1e-5 + 2.0 * (delta / np.where(amin > 0, amin, 1.0)) / ln_ratio
+    rel = np.abs(gpu.astype(np.float64) - ref) / ref
+    bad = well & (rel > tol)
+    assert not bad.any(), f"{what}: k off by {rel[bad].max():.3e} relative in {int(bad.sum())} groups"
+
+
+def assert_step_parity(gpu, ref, v_fmt, what, prev=None):
+    """prev: the state both sides started from (None: a fresh state)."""
+    th_g, st_g = gpu
+    th_r, st_r = ref
+    zeros = np.zeros_like(st_r["m_amax"])
+    prev_m = zeros if prev is None else prev["m_amax"]
+    prev_v = zeros if prev is None else prev["v_amax"]
+    assert_theta(th_g, th_r, what + " theta")
+    fm = assert_codes(st_g["m_codes"], st_r["m_codes"], what + " m codes")
+    fv = assert_codes(st_g["v_codes"], st_r["v_codes"], what + " v codes")
+    assert_amax(st_g["m_amax"], st_r["m_amax"], prev_m, what + " m amax")
+    assert_amax(st_g["v_amax"], st_r["v_amax"], prev_v, what + " v amax")
+    assert_k(st_g["m_k"], st_r["m_k"], st_r["m_amax"], prev_m, "e4m3", what + " m k")
+    assert_k(st_g["v_k"], st_r["v_k"], st_r["v_amax"], prev_v, v_fmt, what + " v k")
+    return fm, fv

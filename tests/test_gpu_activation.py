@@ -1,0 +1,164 @@
+"""GPU parity of Group Scaling and the activation casts against the oracle
+(bit-exact), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from activation_compression_amd import coat, inputs
+from parity import THREADS, dev, flush, host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def act(rows, cols, seed):
+    spec = inputs.ActivationSpec(f"t{rows}x{cols}", rows, cols, seed=seed)
+    return inputs.gen_activation(spec).numpy().view(np.uint16)
+
+
+def norm0(c):
+    c = c.copy()
+    c[(c & 0x7F) == 0] = 0
+    return c
+
+
+def gpu_group_absmax(x, G):
+    rows, cols = x.shape
+    xd = dev(x)
+    partial = torch.empty(rows * cols // G, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1.0, device="cuda")
+    coat.coat_group_absmax(xd, partial, amax, group_size=G)
+    torch.cuda.synchronize()
+    return host(partial), np.float32(host(amax)[0])
+
+
+def test_e4m3_convert_all_bf16_values():
+    """Every finite BF16 value in [-448, 448] through the per-tensor cast with
+    A = 448 (so y = x exactly): the hardware conversion must be OCP E4M3
+    round-to-nearest-even, midpoints included."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    x = bits[keep]
+    x = np.concatenate([x, np.zeros((-x.size) % 16, np.uint16)])
+    flush(f"convert sweep: {x.size} values")
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, device="cuda")
+    amax = torch.tensor([448.0], device="cuda")
+    coat.coat_quant_per_tensor(dev(x), amax, codes, scale)
+    torch.cuda.synchronize()
+    ref, ref_scale = orc.quant_per_tensor(x, 448.0)
+    assert (norm0(host(codes)) == ref).all()
+    assert host(scale)[0] == ref_scale == np.float32(1.0)
+
+
+@pytest.mark.parametrize("G", [32, 128, 512, 1024])
+def test_group_absmax_small(G):
+    x = act(64, 4096, seed=G)
+    partial, amax = gpu_group_absmax(x, G)
+    rp, ra = orc.group_absmax(x, G)
+    assert (partial == rp).all() and amax == ra
+
+
+def test_group_absmax_ragged_rows():
+    # rows * cols not a multiple of the 1024-element wave chunk
+    x = act(3, 96, seed=5)
+    partial, amax = gpu_group_absmax(x, 32)
+    rp, ra = orc.group_absmax(x, 32)
+    assert (partial == rp).all() and amax == ra
+
+
+def test_absmax_reduce_standalone():
+    rng = np.random.default_rng(0)
+    for n in (1, 7, 1000, 300_001):
+        p = (rng.random(n) * 10 ** rng.uniform(-3, 3, n)).astype(np.float32)
+        amax = torch.full((1,), 123.0, device="cuda")
+        coat.coat_absmax_reduce(dev(p), amax)
+        torch.cuda.synchronize()
+        assert host(amax)[0] == orc.absmax_reduce(p), n
+
+
+@pytest.mark.parametrize("rows, cols", [(64, 4096), (5, 1032)])
+def test_per_tensor_cast_small(rows, cols):
+    """Cast with the tensor absmax; (5, 1032) leaves a ragged 8-element tail."""
+    x = act(rows, cols, seed=rows)
+    A = np.float32(np.abs((x.astype(np.uint32) << 16).view(np.float32)).max())
+    codes = torch.empty(rows * cols, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, device="cuda")
+    coat.coat_quant_per_tensor(dev(x), torch.tensor([A], device="cuda"), codes, scale)
+    torch.cuda.synchronize()
+    rc, rs = orc.quant_per_tensor(x, A)
+    assert (norm0(host(codes)) == rc).all() and host(scale)[0] == rs
+
+
+@pytest.mark.parametrize("G", [32, 128, 1024])
+def test_group_cast_small(G):
+    x = act(32, 2048, seed=G + 1)
+    x[5, :G] = 0
+    x[6, G:2 * G] = 0x8000  # negative zeros
+    xd = dev(x)
+    ng = x.size // G
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(ng, device="cuda")
+    partial = torch.empty(ng, device="cuda")
+    coat.coat_quant_group(xd, codes, scales, partial, group_size=G)
+    codes2 = torch.empty_like(codes)
+    scales2 = torch.empty_like(scales)
+    coat.coat_quant_group(xd, codes2, scales2, None, group_size=G)
+    torch.cuda.synchronize()
+    rc, rs, rp = orc.quant_group(x, G)
+    assert (norm0(host(codes)) == rc).all()
+    assert (host(scales) == rs).all() and (host(partial) == rp).all()
+    assert (host(codes2) == host(codes)).all() and (host(scales2) == rs).all()
+
+
+def test_zero_tensor():
+    x = np.zeros((8, 256), np.uint16)
+    x[2, 7] = 0x8000
+    partial, amax = gpu_group_absmax(x, 128)
+    assert amax == 0 and (partial == 0).all()
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, device="cuda")
+    coat.coat_quant_per_tensor(dev(x), torch.zeros(1, device="cuda"), codes, scale)
+    torch.cuda.synchronize()
+    assert host(scale)[0] == 1.0 and (norm0(host(codes)) == 0).all()
+
+
+@pytest.mark.slow
+def test_linear_input_full_size_per_tensor_path():
+    """[16384 x 4096] with an x100 outlier channel: stage 1 -> stage 2 ->
+    per-tensor cast, at full size and in the launch configuration timed."""
+    spec = inputs.linear_input()
+    x = inputs.gen_activation(spec, device="cuda")
+    flush(f"per-tensor path on {spec.name}")
+    partial = torch.empty(spec.numel // 128, device="cuda")
+    amax = torch.empty(1, device="cuda")
+    codes = torch.empty(spec.numel, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, device="cuda")
+    coat.coat_group_absmax(x, partial, amax, group_size=128)
+    coat.coat_quant_per_tensor(x, amax, codes, scale)
+    torch.cuda.synchronize()
+    xh = host(x)
+    rp, ra = orc.group_absmax(xh, 128, threads=THREADS)
+    assert (host(partial) == rp).all() and host(amax)[0] == ra
+    rc, rs = orc.quant_per_tensor(xh, ra, threads=THREADS)
+    assert host(scale)[0] == rs
+    assert (norm0(host(codes)) == rc).all()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["linear", "swiglu"])
+def test_group_cast_full_size(which):
+    spec = inputs.linear_input() if which == "linear" else inputs.swiglu_input()
+    x = inputs.gen_activation(spec, device="cuda")
+    flush(f"1x128 group cast on {spec.name}")
+    ng = spec.numel // 128
+    codes = torch.empty(spec.numel, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(ng, device="cuda")
+    partial = torch.empty(ng, device="cuda")
+    coat.coat_quant_group(x, codes, scales, partial, group_size=128)
+    torch.cuda.synchronize()
+    rc, rs, rp = orc.quant_group(host(x), 128, threads=THREADS)
+    assert (host(scales) == rs).all() and (host(partial) == rp).all()
+    assert (norm0(host(codes)) == rc).all()

@@ -1,0 +1,164 @@
+"""GPU parity of the fused FP8-state AdamW step against the oracle, through
+the C ABI.  Every comparison starts both sides from the same inputs: seeded
+parameters and gradients, and either a fresh state or a state the ORACLE
+produced (never one produced by the GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from activation_compression_amd import coat, inputs
+from parity import (LR, assert_codes, assert_step_parity, assert_theta, dev, flush, gpu_hp, gpu_step,
+                    host, np_state, oracle_step)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def config1_inputs(steps):
+    spec = inputs.single_1024()
+    theta = inputs.gen_params(spec).numpy()
+    grads = [inputs.gen_grads(spec, t).numpy().view(np.uint16) for t in range(1, steps + 1)]
+    return spec, theta, grads
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("G", [32, 64, 128, 256, 512, 1024])
+def test_step1_from_fresh_state(v_fmt, G):
+    spec, theta, (g1,) = config1_inputs(1)
+    flush(f"step 1 {spec.name} G={G} v={v_fmt}")
+    st = np_state(spec.numel, G)
+    gpu = gpu_step(theta, g1, st, G, v_fmt, 1)
+    ref = oracle_step(theta, g1, st, G, v_fmt, 1)
+    assert_step_parity(gpu, ref, v_fmt, f"G={G} {v_fmt}")
+    # closed form of the first update: theta (1 - lr wd) - lr g / (|g| + eps)
+    gd = (g1.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = theta.astype(np.float64) * (1 - LR * np.float32(0.1)) - LR * gd / (np.abs(gd) + np.float32(1e-8))
+    assert_theta(gpu[0], want, "closed form")
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_ten_steps_along_the_oracle_trajectory(v_fmt):
+    """Config 1 (1024x1024, per-row log-normal gradient scale), ten steps.  At
+    every step t the GPU and the oracle both start from the oracle's state
+    after step t-1, so each step is judged on its own."""
+    spec, theta, grads = config1_inputs(10)
+    G = 128
+    st = np_state(spec.numel, G)
+    fracs = []
+    for t in range(1, 11):
+        flush(f"trajectory step {t} v={v_fmt}")
+        gpu = gpu_step(theta, grads[t - 1], st, G, v_fmt, t)
+        ref = oracle_step(theta, grads[t - 1], st, G, v_fmt, t)
+        fracs.append(assert_step_parity(gpu, ref, v_fmt, f"step {t}", prev=st))
+        theta, st = ref
+    flush(f"identical code fraction per step (m, v): {fracs}")
+
+
+def stress_inputs(n, G, v_fmt, steps=2):
+    spec = inputs.stress(G, v_fmt, numel=n)
+    theta = inputs.gen_params(spec).numpy()
+    grads = [inputs.gen_grads(spec, t).numpy().view(np.uint16) for t in range(1, steps + 1)]
+    return spec, theta, grads
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("G", [32, 128, 512])
+def test_stress_two_steps(v_fmt, G):
+    """Gradients over ten decades with 5% zeros: groups wider than the FP8
+    range get k < 1; step 2 dequantizes those states."""
+    spec, theta, grads = stress_inputs(1 << 22, G, v_fmt)
+    st = np_state(spec.numel, G)
+    for t in (1, 2):
+        flush(f"stress step {t} G={G} v={v_fmt}")
+        gpu = gpu_step(theta, grads[t - 1], st, G, v_fmt, t)
+        ref = oracle_step(theta, grads[t - 1], st, G, v_fmt, t)
+        assert_step_parity(gpu, ref, v_fmt, f"stress t={t}", prev=st)
+        theta, st = ref
+    assert (st["m_k"] < 1).any() and (st["m_k"] > 0).all()
+
+
+@pytest.mark.parametrize("n, G", [(32, 32), (96, 32), (5 * 1024 + 64, 64), (3 * 1024 + 512, 512), (1024, 1024)])
+def test_ragged_sizes(n, G):
+    """Sizes that leave partial 1024-element wave chunks, down to one group."""
+    rng = np.random.default_rng(n)
+    theta = rng.normal(0, 0.02, n).astype(np.float32)
+    g = (rng.normal(0, 1e-3, n) * np.exp(rng.normal(0, 1, n))).astype(np.float32)
+    g_bits = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    g2 = torch.from_numpy(rng.normal(0, 1e-3, n).astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    st = np_state(n, G)
+    for t, gb in ((1, g_bits), (2, g2)):
+        gpu = gpu_step(theta, gb, st, G, "e5m2", t)
+        ref = oracle_step(theta, gb, st, G, "e5m2", t, threads=1)
+        assert_step_parity(gpu, ref, "e5m2", f"n={n} t={t}", prev=st)
+        theta, st = ref
+
+
+def test_degenerate_groups():
+    """All-zero gradients (all-zero groups), equal magnitudes (k = 1), a single
+    nonzero per group, and moments decayed to FP32 denormals."""
+    G, n = 128, 128 * 64
+    rng = np.random.default_rng(3)
+    theta = rng.normal(0, 0.02, n).astype(np.float32)
+    g = np.zeros(n, np.float32)
+    g[128:256] = 0.5
+    g[256:384] = np.where(rng.random(128) < 0.5, -0.25, 0.25)
+    g[384 + 7] = -3e-3
+    g[512:] = rng.normal(0, 1e-3, n - 512)
+    g_bits = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    st = np_state(n, G)
+    gpu = gpu_step(theta, g_bits, st, G, "e4m3", 1)
+    ref = oracle_step(theta, g_bits, st, G, "e4m3", 1, threads=1)
+    assert_step_parity(gpu, ref, "e4m3", "degenerate t=1")
+    assert (gpu[1]["m_codes"][:128] & 0x7F == 0).all() and gpu[1]["m_amax"][0] == 0 and gpu[1]["m_k"][0] == 1
+    assert gpu[1]["m_k"][1] == 1 and gpu[1]["m_k"][2] == 1
+    # a state whose m group max is an FP32 denormal, step with zero gradient
+    theta, st = ref
+    st["m_amax"][10:20] = np.float32(3e-39)
+    st["v_amax"][10:20] = np.float32(1e-30)
+    g0 = np.zeros(n, np.uint16)
+    gpu = gpu_step(theta, g0, st, G, "e4m3", 2)
+    ref = oracle_step(theta, g0, st, G, "e4m3", 2, threads=1)
+    assert_step_parity(gpu, ref, "e4m3", "denormal t=2", prev=st)
+
+
+def test_deterministic_bytes():
+    spec, theta, (g1, g2) = config1_inputs(2)
+    st = np_state(spec.numel, 128)
+    a = gpu_step(theta, g1, st, 128, "e4m3", 1)
+    b = gpu_step(theta, g1, st, 128, "e4m3", 1)
+    assert (a[0] == b[0]).all() and all((a[1][k] == b[1][k]).all() for k in st)
+
+
+@pytest.mark.slow
+def test_stress_64mi_launch_config_sampled():
+    """The full 64 Mi stress tensor at the launch configuration the benchmark
+    uses, compared with the oracle on a seeded sample of groups."""
+    G, v_fmt = 128, "e5m2"
+    spec = inputs.stress(G, v_fmt)
+    n = spec.numel
+    theta_d = inputs.gen_params(spec, device="cuda")
+    g_d = inputs.gen_grads(spec, 1, device="cuda")
+    st_d = inputs.fresh_state(n, G, device="cuda")
+    theta0 = host(theta_d)
+    g_h = host(g_d)
+    flush("stress 64Mi full-size step 1")
+    coat.coat_adamw_step(theta_d, g_d, st_d["m_codes"], st_d["m_amax"], st_d["m_k"], st_d["v_codes"],
+                         st_d["v_amax"], st_d["v_k"], group_size=G, v_format=v_fmt, hp=gpu_hp(1))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    groups = np.sort(rng.choice(n // G, 4096, replace=False))
+    idx = (groups[:, None] * G + np.arange(G)).ravel()
+    th_s = np.ascontiguousarray(theta0[idx])
+    st_s = np_state(idx.size, G)
+    ref = oracle_step(th_s, np.ascontiguousarray(g_h[idx]), st_s, G, v_fmt, 1)
+    th_g = host(theta_d)[idx]
+    st_g = {k: host(v) for k, v in st_d.items()}
+    gpu = (th_g, {"m_codes": st_g["m_codes"][idx], "v_codes": st_g["v_codes"][idx],
+                  "m_amax": st_g["m_amax"][groups], "m_k": st_g["m_k"][groups],
+                  "v_amax": st_g["v_amax"][groups], "v_k": st_g["v_k"][groups]})
+    assert_step_parity(gpu, ref, v_fmt, "stress 64Mi sampled")
+    # properties over every element: v codes carry no sign; no NaN code
+    vc = st_g["v_codes"]
+    assert (vc & 0x80 == 0).all() and ((vc & 0x7F) <= 0x7B).all()
+    assert ((st_g["m_codes"] & 0x7F) != 0x7F).all()
