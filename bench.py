@@ -1,0 +1,264 @@
+"""Benchmark: FP8-state AdamW params updated/s and achieved HBM GB/s on one MI355X.
+
+One step is one pass of the whole hot path over synthetic inputs resident in
+HBM:
+  1. the fused FP8-state AdamW step over the OLMo-7B-shaped parameter arena
+     (6 888 095 744 FP32 master weights, BF16 gradients, m and v in E4M3,
+     G = 128) -- one coat_adamw_step launch for the whole arena;
+  2. Group Scaling of a linear-layer input [16384 x 4096]: stage 1 + stage 2
+     (coat_group_absmax) and the per-tensor E4M3 cast (coat_quant_per_tensor);
+  3. 1x128 E4M3 group casts of the same tensor and of a SwiGLU input
+     [16384 x 11008] (coat_quant_group).
+value = parameters updated per second of whole steps.  The roofline entry is
+the dominant kernel, the AdamW step: algorithmic bytes per launch
+(14 + 32/G bytes per parameter) over its average launch time, measured with
+HIP events on the stream it runs on.  The CPU baseline is the oracle on a
+bounded sample of the same step, on the host's cores.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_fp8_step-olmo7b-pmc.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def step_bytes_per_param(G):
+    # theta r+w 8, grad 2, m codes r+w 2, v codes r+w 2, (amax, k) x 2 states r+w per group
+    return 14.0 + 32.0 / G
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("adamw_fp8_step.hip", "device.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "activation_compression_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, acts, G, threads):
+    """The oracle (as it stands) on a bounded sample of one step, scaled to
+    params/s of the whole step.  Sample: the first two tensors of the arena
+    (l0.qkv, l0.out: 67 108 864 parameters) for the AdamW step -- timed on
+    step 2 so that the moments it dequantizes are nonzero -- and the first
+    2048 rows of each activation tensor for Group Scaling and the casts."""
+    import numpy as np
+
+    import oracle as orc
+    from activation_compression_amd import inputs
+
+    n_tensors = 2
+    sub = inputs.ArenaSpec(spec.name + "-sample", spec.config, spec.tensors[:n_tensors], spec.v_fmt, G,
+                           spec.grad_scale)
+    n = sub.numel
+    theta = inputs.gen_params(sub).numpy()
+    st = {k: v.numpy() for k, v in inputs.fresh_state(n, G).items()}
+    f32 = lambda v: float(np.float32(v))
+    hp = lambda t: orc.hparams(f32(inputs.LR), f32(inputs.BETA1), f32(inputs.BETA2), f32(inputs.EPS),
+                               f32(inputs.WEIGHT_DECAY), t)
+    g1 = inputs.gen_grads(sub, 1).numpy().view(np.uint16)
+    g2 = inputs.gen_grads(sub, 2).numpy().view(np.uint16)
+    args = lambda: (theta, None, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"], st["v_k"])
+    a = list(args()); a[1] = g1
+    orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(1), threads=threads)
+    a = list(args()); a[1] = g2
+    t0 = time.perf_counter()
+    orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(2), threads=threads)
+    t_step = (time.perf_counter() - t0) * spec.numel / n
+
+    t_act = 0.0
+    rows = 2048
+    for i, act in enumerate(acts):
+        x = inputs.gen_activation(inputs.ActivationSpec(act.name, rows, act.cols, act.seed)).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        if i == 0:
+            _, amax = orc.group_absmax(x, G, threads=threads)
+            orc.quant_per_tensor(x, amax, threads=threads)
+        orc.quant_group(x, G, threads=threads)
+        t_act += (time.perf_counter() - t0) * act.rows / rows
+    total = t_step + t_act
+    return {
+        "value": spec.numel / total,
+        "unit": "params/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"AdamW step 2 on the first {n_tensors} tensors of the arena ({n} params, scaled x"
+                   f"{spec.numel / n:.1f}); Group Scaling + casts on the first {rows} rows of each "
+                   f"activation tensor (scaled); binary64 C oracle, {threads} threads"),
+        "seconds_per_step": total,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of a known size (to scale the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from activation_compression_amd import coat, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = 4 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": nbytes,
+                          "copy_calibration_bytes_written_per_launch": nbytes, "launches": 3}), flush=True)
+        return
+    coat.lib()
+    spec = inputs.olmo_7b()
+    G = spec.group_size
+    n = spec.numel
+    acts = [inputs.linear_input(), inputs.swiglu_input()]
+
+    log(f"allocating {spec.name}: {n} params")
+    theta = inputs.gen_params(spec, device="cuda")
+    grad = inputs.gen_grads(spec, 1, device="cuda")
+    st = inputs.fresh_state(n, G, device="cuda")
+    xs = [inputs.gen_activation(a, device="cuda") for a in acts]
+    partial = torch.empty(acts[0].numel // G, device="cuda")
+    amax = torch.empty(1, device="cuda")
+    codes_pt = torch.empty(acts[0].numel, dtype=torch.uint8, device="cuda")
+    scale_pt = torch.empty(1, device="cuda")
+    gcodes = [torch.empty(a.numel, dtype=torch.uint8, device="cuda") for a in acts]
+    gscales = [torch.empty(a.numel // G, device="cuda") for a in acts]
+    torch.cuda.synchronize()
+
+    f = lambda v: float(v)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step(t, marks=None):
+        hp = coat.adamw_hparams(f(inputs.LR), f(inputs.BETA1), f(inputs.BETA2), f(inputs.EPS),
+                                f(inputs.WEIGHT_DECAY), t)
+        if marks: marks[0].record()
+        coat.coat_adamw_step(theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"],
+                             st["v_k"], group_size=G, v_format=spec.v_fmt, hp=hp)
+        if marks: marks[1].record()
+        coat.coat_group_absmax(xs[0], partial, amax, group_size=G)
+        if marks: marks[2].record()
+        coat.coat_quant_per_tensor(xs[0], amax, codes_pt, scale_pt)
+        if marks: marks[3].record()
+        coat.coat_quant_group(xs[0], gcodes[0], gscales[0], None, group_size=G)
+        if marks: marks[4].record()
+        coat.coat_quant_group(xs[1], gcodes[1], gscales[1], None, group_size=G)
+        if marks: marks[5].record()
+
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        one_step(step)
+    torch.cuda.synchronize()
+
+    marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    start, stop = ev(), ev()
+    start.record()
+    for i in range(args.steps):
+        step += 1
+        one_step(step, marks[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    names = ["adamw_fp8_step", "group_absmax", "quant_per_tensor", "quant_group_linear", "quant_group_swiglu"]
+    per = {nm: sum(m[j].elapsed_time(m[j + 1]) for m in marks) / args.steps for j, nm in enumerate(names)}
+    bpp = step_bytes_per_param(G)
+    alg = {
+        "adamw_fp8_step": n * bpp,
+        "group_absmax": acts[0].numel * 2 + 2 * 4 * acts[0].numel / G,
+        "quant_per_tensor": acts[0].numel * 3,
+        "quant_group_linear": acts[0].numel * 3 + 4 * acts[0].numel / G,
+        "quant_group_swiglu": acts[1].numel * 3 + 4 * acts[1].numel / G,
+    }
+    kernels = {nm: {"ms": round(per[nm], 4), "algorithmic_bytes": int(alg[nm]),
+                    "gb_per_s": round(alg[nm] / (per[nm] * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(alg[nm] / (per[nm] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)} for nm in names}
+    achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        log(f"timing the oracle on a bounded sample with {threads} threads")
+        cpu = cpu_baseline(spec, acts, G, threads)
+
+    out = {
+        "metric": "FP8-state AdamW params updated/s + achieved HBM GB/s (% of peak), 1xMI355X",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; OLMo-7B-shaped parameter arena and activation shapes, no trained weights)",
+        "config": {
+            "workload": ("olmo-7b-shaped FP8-state AdamW step (6888095744 params, m e4m3, v e4m3, G 128) "
+                         "+ Group Scaling and E4M3 casts of [16384x4096] and [16384x11008] BF16 activations"),
+            "params": n, "group_size": G, "m_format": "e4m3", "v_format": spec.v_fmt,
+            "activations": [[a.rows, a.cols] for a in acts],
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "adamw_fp8_step",
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(alg["adamw_fp8_step"]),
+        },
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "step_hbm_gb_per_s": round(sum(alg.values()) / (ms_per_step * 1e-3) / 1e9, 1),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
