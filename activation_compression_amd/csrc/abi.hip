@@ -3,6 +3,7 @@
 // argument is valid; no device memory is allocated; no call synchronizes.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -17,8 +18,8 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_group(int32_t G) { return G >= 32 && G <= 1024 && (G & (G - 1)) == 0; }
 
-// Workgroups resident at once: CUs x 8, looked up once per device.
-int grid_cap() {
+// Compute units of the current device, looked up once per device.
+int num_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -29,9 +30,8 @@ int grid_cap() {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    const int v = cus * 8;
-    if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
-    return v;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 coat_status from_hip(hipError_t e) { return e == hipSuccess ? COAT_OK : COAT_ERR_HIP; }
@@ -89,7 +89,9 @@ coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16, uint8_t *m_
     // log2 of each format's range MAX / smallest subnormal
     a.m_log2_range = (float)(log2(448.0) + 9.0);
     a.v_log2_range = v_format == COAT_FP8_E5M2 ? (float)(log2(57344.0) + 16.0) : a.m_log2_range;
-    return from_hip(coat::launch_adamw_fp8_step(a, group_size, (int)v_format, (hipStream_t)stream, grid_cap()));
+    memcpy(a.log_tab[0], coat::fp8_log_table(COAT_FP8_E4M3), sizeof a.log_tab[0]);
+    memcpy(a.log_tab[1], coat::fp8_log_table((int)v_format), sizeof a.log_tab[1]);
+    return from_hip(coat::launch_adamw_fp8_step(a, group_size, (int)v_format, (hipStream_t)stream, num_cus()));
 }
 
 coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t group_size,
@@ -99,14 +101,14 @@ coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
     if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_group_absmax(x_bf16, rows * cols, group_size, partial_amax, amax,
-                                              (hipStream_t)stream, grid_cap()));
+                                              (hipStream_t)stream, num_cus()));
 }
 
 coat_status coat_absmax_reduce(const float *partial, int64_t n, float *amax, void *stream) {
     if (!partial || !amax) return COAT_ERR_NULL;
     if (!aligned(partial, 4) || !aligned(amax, 4)) return COAT_ERR_ALIGN;
     if (n <= 0) return COAT_ERR_SHAPE;
-    return from_hip(coat::launch_absmax_reduce(partial, n, amax, (hipStream_t)stream, grid_cap()));
+    return from_hip(coat::launch_absmax_reduce(partial, n, amax, (hipStream_t)stream, num_cus()));
 }
 
 coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float *amax, uint8_t *codes,
@@ -116,7 +118,7 @@ coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float
         return COAT_ERR_ALIGN;
     if (n <= 0 || n % 8 != 0) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_quant_per_tensor(x_bf16, n, amax, codes, scale, (hipStream_t)stream,
-                                                  grid_cap()));
+                                                  num_cus()));
 }
 
 coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t group_size,
@@ -128,7 +130,7 @@ coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
     if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_quant_group(x_bf16, rows * cols, group_size, codes, scales,
-                                             partial_amax_or_null, (hipStream_t)stream, grid_cap()));
+                                             partial_amax_or_null, (hipStream_t)stream, num_cus()));
 }
 
 }  // extern "C"

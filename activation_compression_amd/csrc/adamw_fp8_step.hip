@@ -34,195 +34,269 @@ namespace {
 
 constexpr float kLn2 = 0.693147180559945309417f;
 
-// log2(|decode(c)| / MAX) for code magnitude c, split into hi + lo FP32.
-template <int F>
-__device__ float2 log_table_entry(uint32_t c) {
-    const float d = decode1<F>(c);
-    if (c == 0 || !(d > 0.0f) || !__builtin_isfinite(d))
-        return make_float2(-0x1p100f, 0.0f);
-    const double L = log2((double)d) - log2((double)Fp8<F>::kMax);
-    const float hi = (float)L;
-    return make_float2(hi, (float)(L - (double)hi));
-}
+// log2(MAX) rounded to FP32 (folded into the exp2 argument of requantization).
+template <int F> struct Log2Max;
+template <> struct Log2Max<kE4M3> { static constexpr float v = 8.80735492205760410744f; };
+template <> struct Log2Max<kE5M2> { static constexpr float v = 15.80735492205760410744f; };
 
-// 1/k as hi + lo: hi = RN(1/k), lo = hi * (1 - k hi) (the FMA residual is exact).
+// 1/k as hi + lo: hi ~ 1/k (native reciprocal), lo = hi (1 - k hi) (the FMA
+// residual is exact), so hi + lo = 1/k to second order in the residual.
 __device__ __forceinline__ void recip2(float k, float &hi, float &lo) {
-    hi = 1.0f / k;
+    hi = __builtin_amdgcn_rcpf(k);
     lo = __builtin_fmaf(-k, hi, 1.0f) * hi;
 }
 
-// Inverse expansion of one code with its group's (amax, 1/k = ih + il).
-__device__ __forceinline__ float dequant(uint32_t code, const float2 *tab, float amax,
+// RN(1/b) for a normal b with a normal reciprocal: native reciprocal plus one
+// Newton step.
+__device__ __forceinline__ float rcp_rn(float b) {
+    const float y = __builtin_amdgcn_rcpf(b);
+    return __builtin_fmaf(__builtin_fmaf(-b, y, 1.0f), y, y);
+}
+
+// Inverse expansion of one code with its group's amax and 1/k = ih + il:
+// amax 2^(L/k) = amax 2^ph 2^pl ~ 2^ph (amax + amax ln2 pl).
+template <bool kSigned>
+__device__ __forceinline__ float dequant(uint32_t byte, const float2 *tab, float amax, float amax_ln2,
                                          float ih, float il) {
-    const float2 L = tab[code & 0x7Fu];
+    const float2 L = tab[byte];
     const float ph = L.x * ih;
     float pl = __builtin_fmaf(L.x, ih, -ph);  // exact rounding error of ph
     pl = __builtin_fmaf(L.x, il, pl);
     pl = __builtin_fmaf(L.y, ih, pl);
-    const float ea = __builtin_amdgcn_exp2f(ph) * amax;
-    const float mag = __builtin_fmaf(ea, pl * kLn2, ea);  // 2^pl ~ 1 + pl ln 2
-    return __uint_as_float(__float_as_uint(mag) | ((code & 0x80u) << 24));
+    const float mag = __builtin_amdgcn_exp2f(ph) * __builtin_fmaf(amax_ln2, pl, amax);
+    if constexpr (kSigned)
+        return __uint_as_float(__float_as_uint(mag) | ((byte & 0x80u) << 24));
+    return mag;
 }
 
-// Per-group quantization parameters of a new moment.
+// Per-group quantization parameters of one new moment.
 struct GroupQ {
-    float amax;    // stored scale: the group's max |x|
-    float k;       // stored expansion exponent
-    float amax_s;  // amax * 2^sh, in [1, 2)
-    float inv_s;   // RN(1 / amax_s)
-    int sh;
+    float amax;   // stored scale: the group's max |x|
+    float k;      // stored expansion exponent
+    float amq;    // amax, or amax 2^sh in [1, 2) for groups outside [2^-120, 2^120]
+    float invq;   // RN(1 / amq)
+    int sh;       // prescale exponent (0 on the common path)
 };
 
 // mx: bits of max |x|; mn: bits of min nonzero |x| (0 when none).
 __device__ __forceinline__ GroupQ group_q(uint32_t mx, uint32_t mn, float log2_range) {
     GroupQ q;
     q.amax = __uint_as_float(mx);
-    if (mx == 0u) {
-        q.k = 1.0f; q.amax_s = 1.0f; q.inv_s = 1.0f; q.sh = 0;
-        return q;
-    }
+    q.k = 1.0f; q.amq = 1.0f; q.invq = 1.0f; q.sh = 0;
+    if (mx == 0u) return q;  // all-zero group: every code is 0
     int ea;
-    const float ma = frexpf(q.amax, &ea);  // amax = ma 2^ea, ma in [0.5, 1)
-    q.sh = 1 - ea;
-    q.amax_s = 2.0f * ma;
-    q.inv_s = 1.0f / q.amax_s;
-    if (mn == mx) {
-        q.k = 1.0f;  // all nonzero magnitudes equal: ln R = 0
+    const float ma = __builtin_amdgcn_frexp_mantf(q.amax);  // [0.5, 1)
+    ea = __builtin_amdgcn_frexp_expf(q.amax);
+    if (mx < 0x03800000u || mx > 0x7B800000u) {  // outside [2^-120, 2^120]
+        q.sh = 1 - ea;
+        q.amq = 2.0f * ma;
     } else {
-        int eb;
-        const float mb = frexpf(__uint_as_float(mn), &eb);
-        // log2(amax / amin) without overflow for any FP32 pair
-        const float lg = (float)(ea - eb) + log2f(ma / mb);
-        q.k = log2_range / lg;  // (amax/amin)^k spans MAX / min_subnormal
+        q.amq = q.amax;
+    }
+    q.invq = rcp_rn(q.amq);
+    if (mn != mx) {
+        const float mb = __builtin_amdgcn_frexp_mantf(__uint_as_float(mn));
+        const int eb = __builtin_amdgcn_frexp_expf(__uint_as_float(mn));
+        // log2(amax / amin) = (ea - eb) + log2(ma / mb), the quotient correctly rounded
+        const float ratio = div_rn_from_rcp(ma, mb, rcp_rn(mb));
+        const float lg = (float)(ea - eb) + __builtin_amdgcn_logf(ratio);
+        // k = log2(R_fmt) / log2(amax / amin): (amax/amin)^k spans MAX / min_subnormal
+        q.k = div_rn_from_rcp(log2_range, lg, rcp_rn(lg));
     }
     return q;
 }
 
-// sign(x) * min(MAX (|x| / amax)^k, MAX), ready for the FP8 convert.
+// Broadcast lane J of every aligned run of W lanes to the whole run.
+template <int W, int J>
+__device__ __forceinline__ float run_bcast(float v) {
+    const int x = __float_as_int(v);
+    int r;
+    if constexpr (W == 2)
+        r = __builtin_amdgcn_mov_dpp(x, J == 0 ? 0xA0 : 0xF5, 0xF, 0xF, true);  // quad_perm [J,J,J+2,J+2]
+    else if constexpr (W == 4)
+        r = __builtin_amdgcn_mov_dpp(x, J == 0 ? 0x00 : 0x55, 0xF, 0xF, true);  // quad_perm [J,J,J,J]
+    else if constexpr (W <= 32)
+        r = __builtin_amdgcn_ds_swizzle(x, ((J & 0x1F) << 5) | (0x1F & ~(W - 1)));  // (lane & ~(W-1)) | J
+    else
+        r = __shfl(x, J);
+    return __int_as_float(r);
+}
+
+// sign(x) min(MAX (|x| / amax)^k, MAX) with the group's (amq, invq, k);
+// xs is |x| on the common path, |x| 2^sh on the prescaled one.
 template <int F>
-__device__ __forceinline__ float expand(float x, const GroupQ &q) {
-    const float xs = __builtin_amdgcn_ldexpf(__builtin_fabsf(x), q.sh);
-    const float r = div_rn_from_rcp(xs, q.amax_s, q.inv_s);
-    float y = __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(r) * q.k) * Fp8<F>::kMax;
-    y = __builtin_fminf(y, Fp8<F>::kMax);
-    return with_sign_of(y, x);
+__device__ __forceinline__ float expand(float xs, float amq, float invq, float k) {
+    const float r = div_rn_from_rcp(xs, amq, invq);  // RN(|x| / amax) <= 1
+    const float y = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_amdgcn_logf(r), k, Log2Max<F>::v));
+    return __builtin_fminf(y, Fp8<F>::kMax);
+}
+
+// One wave's pass over 1024 consecutive parameters starting at `base` (wave-
+// uniform).  kTail: the last, partial chunk -- lanes past n load nothing and
+// store nothing (their whole groups are past n as well, since n % G == 0).
+template <int G, int VF, bool kTail>
+__device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab, int64_t base, int lane) {
+    constexpr int LPG = G / 16;  // lanes per group (2 .. 64)
+    const int j = lane & (LPG - 1);
+    const bool v_lane = j == 1;  // lane 0 of a group computes m's parameters, lane 1 v's
+    const bool act = !kTail || base + lane * 16 < a.n;
+    const int64_t gbase = base / G;  // first group of the chunk
+    const int lgrp = lane / LPG;     // this lane's group within the chunk
+
+    // wave-uniform bases, per-lane constant offsets
+    const float *pth = a.param + base;
+    const uint16_t *pg = a.grad + base;
+    const uint8_t *pmc = a.m_codes + base;
+    const uint8_t *pvc = a.v_codes + base;
+
+    float th[16];
+    uint32_t gw[8], mw[4], vw[4];
+    float am_m = 0.0f, k_m = 1.0f, am_v = 0.0f, k_v = 1.0f;
+    if (act) {
+        const float4 *pp = reinterpret_cast<const float4 *>(pth) + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 t = pp[i];
+            th[4 * i] = t.x; th[4 * i + 1] = t.y; th[4 * i + 2] = t.z; th[4 * i + 3] = t.w;
+        }
+        const uint4 *gp = reinterpret_cast<const uint4 *>(pg) + lane * 2;
+        const uint4 g0 = gp[0], g1 = gp[1];
+        gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
+        gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
+        const uint4 mc = reinterpret_cast<const uint4 *>(pmc)[lane];
+        const uint4 vc = reinterpret_cast<const uint4 *>(pvc)[lane];
+        mw[0] = mc.x; mw[1] = mc.y; mw[2] = mc.z; mw[3] = mc.w;
+        vw[0] = vc.x; vw[1] = vc.y; vw[2] = vc.z; vw[3] = vc.w;
+        am_m = a.m_amax[gbase + lgrp]; k_m = a.m_k[gbase + lgrp];
+        am_v = a.v_amax[gbase + lgrp]; k_v = a.v_k[gbase + lgrp];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) th[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gw[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { mw[i] = 0u; vw[i] = 0u; }
+    }
+
+    float ihm, ilm, ihv, ilv;
+    recip2(k_m, ihm, ilm);
+    recip2(k_v, ihv, ilv);
+    const float am_m_ln2 = am_m * kLn2, am_v_ln2 = am_v * kLn2;
+
+    // dequantize, AdamW in FP32, group statistics of the new moments
+    float m1[16], v1[16];
+    float mx_m = 0.0f, mx_v = 0.0f;
+    uint32_t mn_m = ~0u, mn_v = ~0u;  // min over the bits of 2|x| - 2: zero wraps to the top
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t cm = (mw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const uint32_t cv = (vw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const float m0 = dequant<true>(cm, tab, am_m, am_m_ln2, ihm, ilm);
+        const float v0 = dequant<false>(cv, tab + 256, am_v, am_v_ln2, ihv, ilv);
+        const float g = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
+
+        const float m = __builtin_fmaf(a.beta1, m0, a.omb1 * g);
+        const float v = __builtin_fmaf(a.beta2, v0, a.omb2 * (g * g));
+        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(v), a.inv_sqrt_bc2, a.eps);
+        const float u = m * __builtin_amdgcn_rcpf(den);
+        th[i] = __builtin_fmaf(th[i], a.decay, -a.step_size * u);
+        m1[i] = m;
+        v1[i] = v;
+
+        mx_m = __builtin_fmaxf(mx_m, __builtin_fabsf(m));
+        mx_v = __builtin_fmaxf(mx_v, v);
+        mn_m = min(mn_m, (__float_as_uint(m) << 1) - 2u);
+        mn_v = min(mn_v, (__float_as_uint(v) << 1) - 2u);
+    }
+    if (act) {
+        float4 *pp = reinterpret_cast<float4 *>(a.param + base) + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
+    }
+
+    // group statistics (non-negative floats order like their bit patterns)
+    const uint32_t gx_m = run_max<LPG>(__float_as_uint(mx_m));
+    const uint32_t gx_v = run_max<LPG>(__float_as_uint(mx_v));
+    const uint32_t gn_m = (run_min<LPG>(mn_m) + 2u) >> 1;
+    const uint32_t gn_v = (run_min<LPG>(mn_v) + 2u) >> 1;
+
+    // one evaluation per lane: lane 0 of a group for m, lane 1 for v, then broadcast
+    const GroupQ q = group_q(v_lane ? gx_v : gx_m, v_lane ? gn_v : gn_m,
+                             v_lane ? a.v_log2_range : a.m_log2_range);
+    if (act && j < 2) {
+        (v_lane ? a.v_amax : a.m_amax)[gbase + lgrp] = q.amax;
+        (v_lane ? a.v_k : a.m_k)[gbase + lgrp] = q.k;
+    }
+    const float amq_m = run_bcast<LPG, 0>(q.amq), inv_m = run_bcast<LPG, 0>(q.invq);
+    const float kq_m = run_bcast<LPG, 0>(q.k);
+    const float amq_v = run_bcast<LPG, 1>(q.amq), inv_v = run_bcast<LPG, 1>(q.invq);
+    const float kq_v = run_bcast<LPG, 1>(q.k);
+    const int sh_m = __float_as_int(run_bcast<LPG, 0>(__int_as_float(q.sh)));
+    const int sh_v = __float_as_int(run_bcast<LPG, 1>(__int_as_float(q.sh)));
+
+    uint32_t om[4], ov[4];
+    if ((sh_m | sh_v) == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float ym[4], yv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float xm = m1[4 * t + u];
+                ym[u] = with_sign_of(expand<kE4M3>(__builtin_fabsf(xm), amq_m, inv_m, kq_m), xm);
+                yv[u] = expand<VF>(v1[4 * t + u], amq_v, inv_v, kq_v);
+            }
+            om[t] = cvt4<kE4M3>(ym[0], ym[1], ym[2], ym[3]);
+            ov[t] = cvt4<VF>(yv[0], yv[1], yv[2], yv[3]);
+        }
+    } else {  // a group max outside [2^-120, 2^120]: power-of-two prescale first
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float ym[4], yv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float xm = m1[4 * t + u];
+                ym[u] = with_sign_of(expand<kE4M3>(__builtin_amdgcn_ldexpf(__builtin_fabsf(xm), sh_m),
+                                                   amq_m, inv_m, kq_m), xm);
+                yv[u] = expand<VF>(__builtin_amdgcn_ldexpf(v1[4 * t + u], sh_v), amq_v, inv_v, kq_v);
+            }
+            om[t] = cvt4<kE4M3>(ym[0], ym[1], ym[2], ym[3]);
+            ov[t] = cvt4<VF>(yv[0], yv[1], yv[2], yv[3]);
+        }
+    }
+    if (act) {
+        reinterpret_cast<uint4 *>(a.m_codes + base)[lane] = make_uint4(om[0], om[1], om[2], om[3]);
+        reinterpret_cast<uint4 *>(a.v_codes + base)[lane] = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+    }
 }
 
 template <int G, int VF>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a) {
-    __shared__ float2 tab[256];  // [0, 128): m codes (E4M3); [128, 256): v codes
+    // Per code byte (both signs): [0, 256) m codes (E4M3), [256, 512) v codes.
+    __shared__ float2 tab[512];
     {
         const uint32_t t = threadIdx.x;
-        tab[t] = t < 128 ? log_table_entry<kE4M3>(t) : log_table_entry<VF>(t - 128);
+        tab[t] = a.log_tab[0][t & 127u];
+        tab[256 + t] = a.log_tab[1][t & 127u];
     }
     __syncthreads();
 
-    constexpr int LPG = G / 16;  // lanes per group
     const int lane = threadIdx.x & 63;
-    const bool leader = (lane % LPG) == 0;
-    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
-
-    for (int64_t chunk = wave0; chunk < a.n_chunks; chunk += wstride) {
-        const int64_t e0 = chunk * kWaveElems + lane * 16;
-        const bool act = e0 < a.n;  // n % 32 == 0: a lane is all in or all out
-        const int64_t grp = e0 / G;
-
-        float th[16];
-        uint32_t gw[8], mw[4], vw[4];
-        float am_m = 0.0f, k_m = 1.0f, am_v = 0.0f, k_v = 1.0f;
-        if (act) {
-            const float4 *pp = reinterpret_cast<const float4 *>(a.param + e0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 t = pp[i];
-                th[4 * i] = t.x; th[4 * i + 1] = t.y; th[4 * i + 2] = t.z; th[4 * i + 3] = t.w;
-            }
-            const uint4 *gp = reinterpret_cast<const uint4 *>(a.grad + e0);
-            const uint4 g0 = gp[0], g1 = gp[1];
-            gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
-            gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
-            const uint4 mc = *reinterpret_cast<const uint4 *>(a.m_codes + e0);
-            const uint4 vc = *reinterpret_cast<const uint4 *>(a.v_codes + e0);
-            mw[0] = mc.x; mw[1] = mc.y; mw[2] = mc.z; mw[3] = mc.w;
-            vw[0] = vc.x; vw[1] = vc.y; vw[2] = vc.z; vw[3] = vc.w;
-            am_m = a.m_amax[grp]; k_m = a.m_k[grp];
-            am_v = a.v_amax[grp]; k_v = a.v_k[grp];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) th[i] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) gw[i] = 0u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { mw[i] = 0u; vw[i] = 0u; }
-        }
-
-        float ihm, ilm, ihv, ilv;
-        recip2(k_m, ihm, ilm);
-        recip2(k_v, ihv, ilv);
-
-        // dequantize, AdamW in FP32, group statistics of the new moments
-        float m1[16], v1[16];
-        uint32_t mx_m = 0u, mn_m = ~0u, mx_v = 0u, mn_v = ~0u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t cm = (mw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            const uint32_t cv = (vw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            const float m0 = dequant(cm, tab, am_m, ihm, ilm);
-            const float v0 = dequant(cv, tab + 128, am_v, ihv, ilv);
-            const float g = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
-
-            const float m = __builtin_fmaf(a.beta1, m0, a.omb1 * g);
-            const float v = __builtin_fmaf(a.beta2, v0, a.omb2 * (g * g));
-            const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(v), a.inv_sqrt_bc2, a.eps);
-            const float u = m * __builtin_amdgcn_rcpf(den);
-            th[i] = __builtin_fmaf(th[i], a.decay, -a.step_size * u);
-            m1[i] = m;
-            v1[i] = v;
-
-            const uint32_t bm = __float_as_uint(m) & 0x7FFFFFFFu;
-            const uint32_t bv = __float_as_uint(v) & 0x7FFFFFFFu;
-            mx_m = max(mx_m, bm); mn_m = min(mn_m, bm - 1u);  // zero wraps to ~0
-            mx_v = max(mx_v, bv); mn_v = min(mn_v, bv - 1u);
-        }
-        if (act) {
-            float4 *pp = reinterpret_cast<float4 *>(a.param + e0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
-        }
-
-        mx_m = run_max<LPG>(mx_m); mn_m = run_min<LPG>(mn_m);
-        mx_v = run_max<LPG>(mx_v); mn_v = run_min<LPG>(mn_v);
-        const GroupQ qm = group_q(mx_m, mn_m + 1u, a.m_log2_range);
-        const GroupQ qv = group_q(mx_v, mn_v + 1u, a.v_log2_range);
-
-        uint32_t om[4], ov[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            om[j] = cvt4<kE4M3>(expand<kE4M3>(m1[4 * j], qm), expand<kE4M3>(m1[4 * j + 1], qm),
-                                expand<kE4M3>(m1[4 * j + 2], qm), expand<kE4M3>(m1[4 * j + 3], qm));
-            ov[j] = cvt4<VF>(expand<VF>(v1[4 * j], qv), expand<VF>(v1[4 * j + 1], qv),
-                             expand<VF>(v1[4 * j + 2], qv), expand<VF>(v1[4 * j + 3], qv));
-        }
-        if (act) {
-            *reinterpret_cast<uint4 *>(a.m_codes + e0) = make_uint4(om[0], om[1], om[2], om[3]);
-            *reinterpret_cast<uint4 *>(a.v_codes + e0) = make_uint4(ov[0], ov[1], ov[2], ov[3]);
-            if (leader) {
-                a.m_amax[grp] = qm.amax; a.m_k[grp] = qm.k;
-                a.v_amax[grp] = qv.amax; a.v_k[grp] = qv.k;
-            }
-        }
-    }
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) +
+                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (chunk >= a.n_chunks) return;
+    if (chunk < a.n / kWaveElems)  // every lane in range
+        step_chunk<G, VF, false>(a, tab, chunk * kWaveElems, lane);
+    else
+        step_chunk<G, VF, true>(a, tab, chunk * kWaveElems, lane);
 }
 
 template <int G, int VF>
-hipError_t launch(const StepArgs &a, hipStream_t stream, int grid_cap) {
-    const int64_t blocks = ceil_div(a.n_chunks, kBlock / 64);
-    const dim3 grid((unsigned)(blocks < grid_cap ? blocks : grid_cap)), block(kBlock);
+hipError_t launch(const StepArgs &a, hipStream_t stream, int num_cus) {
+    constexpr auto kernel = &adamw_fp8_step_kernel<G, VF>;
+    const dim3 grid((unsigned)ceil_div(a.n_chunks, kBlock / 64));
     void *args[] = {const_cast<StepArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&adamw_fp8_step_kernel<G, VF>),
-                           grid, block, args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
 }
 
 template <int VF>
@@ -240,10 +314,38 @@ hipError_t launch_g(const StepArgs &a, int G, hipStream_t s, int cap) {
 
 }  // namespace
 
+// Host side: the dequantization table of each format, built once.
+static void build_log_table(int fmt, float2 *tab) {
+    const int mbits = fmt == kE5M2 ? 2 : 3;
+    const int bias = fmt == kE5M2 ? 15 : 7;
+    const double vmax = fmt == kE5M2 ? 57344.0 : 448.0;
+    for (int c = 0; c < 128; ++c) {
+        const int e = c >> mbits, m = c & ((1 << mbits) - 1);
+        const bool special = fmt == kE5M2 ? e == 31 : (e == 15 && m == 7);
+        if (c == 0 || special) {
+            tab[c] = make_float2(-0x1p100f, 0.0f);  // 2^(-2^100 / k) is exactly 0
+            continue;
+        }
+        const double d = e == 0 ? ldexp((double)m, 1 - bias - mbits)
+                                : ldexp((double)((1 << mbits) | m), e - bias - mbits);
+        const double L = log2(d) - log2(vmax);
+        const float hi = (float)L;
+        tab[c] = make_float2(hi, (float)(L - (double)hi));
+    }
+}
+
+const float2 *fp8_log_table(int fmt) {
+    static const struct Tables {
+        float2 t[2][128];
+        Tables() { build_log_table(kE4M3, t[0]); build_log_table(kE5M2, t[1]); }
+    } tables;
+    return tables.t[fmt == kE5M2 ? 1 : 0];
+}
+
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
-                                 hipStream_t stream, int grid_cap) {
-    return v_format == kE5M2 ? launch_g<kE5M2>(a, group_size, stream, grid_cap)
-                             : launch_g<kE4M3>(a, group_size, stream, grid_cap);
+                                 hipStream_t stream, int num_cus) {
+    return v_format == kE5M2 ? launch_g<kE5M2>(a, group_size, stream, num_cus)
+                             : launch_g<kE4M3>(a, group_size, stream, num_cus);
 }
 
 }  // namespace coat

@@ -8,7 +8,8 @@
 // one scale per 1xG slice along the channel axis.
 //
 // All kernels are HBM-streaming: each lane owns 16 consecutive BF16 values
-// (two 16-byte loads) and writes 16 codes with one 16-byte store.  |x| maxima
+// (two 16-byte loads) and writes 16 codes with one 16-byte store; each wave
+// handles one 1024-element chunk.  |x| maxima
 // are integer maxima of the BF16 bit patterns with the sign cleared (two per
 // v_pk_max_u16), which is exact for every finite value, denormals included.
 // A 1xG slice is G/16 adjacent lanes, reduced with DPP.
@@ -82,9 +83,8 @@ __global__ __launch_bounds__(kBlock) void absmax_stage1_kernel(const uint16_t *_
     constexpr int LPG = G / 16;
     if (blockIdx.x == 0 && threadIdx.x == 0) *amax = 0.0f;
     const int lane = threadIdx.x & 63;
-    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
-    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
+    if (chunk < n_chunks) {
         const int64_t e0 = chunk * kWaveElems + lane * 16;
         const bool act = e0 < n;
         uint32_t m = 0u;
@@ -130,9 +130,8 @@ __global__ __launch_bounds__(kBlock) void quant_per_tensor_kernel(const uint16_t
     const CastQ q = cast_q(A);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = A > 0.0f ? A / 448.0f : 1.0f;
     const int lane = threadIdx.x & 63;
-    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
-    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
+    if (chunk < n_chunks) {
         const int64_t e0 = chunk * kWaveElems + lane * 16;
         if (e0 + 16 <= n) {
             uint32_t w[8];
@@ -157,9 +156,8 @@ __global__ __launch_bounds__(kBlock) void quant_group_kernel(const uint16_t *__r
                                                              float *__restrict__ partial) {
     constexpr int LPG = G / 16;
     const int lane = threadIdx.x & 63;
-    const int64_t wave0 = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
-    for (int64_t chunk = wave0; chunk < n_chunks; chunk += wstride) {
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
+    if (chunk < n_chunks) {
         const int64_t e0 = chunk * kWaveElems + lane * 16;
         const bool act = e0 < n;
         uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
@@ -179,65 +177,79 @@ __global__ __launch_bounds__(kBlock) void quant_group_kernel(const uint16_t *__r
     }
 }
 
-dim3 grid_for(int64_t n_chunks, int grid_cap) {
-    const int64_t blocks = ceil_div(n_chunks, kBlock / 64);
-    return dim3((unsigned)(blocks < grid_cap ? blocks : grid_cap));
-}
-
 template <typename K, typename... Args>
 hipError_t launch_k(K kernel, dim3 grid, hipStream_t s, Args... args) {
     void *ptrs[] = {static_cast<void *>(&args)...};
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), ptrs, 0, s);
 }
 
+// One 1024-element chunk per wave.
+template <auto Kernel>
+dim3 chunk_grid(int64_t n_chunks, int /*num_cus*/) {
+    return dim3((unsigned)ceil_div(n_chunks, kBlock / 64));
+}
+
+template <int G>
+hipError_t launch_stage1(const uint16_t *x, int64_t n, int64_t nc, float *partial, float *amax, hipStream_t s,
+                         int num_cus) {
+    constexpr auto k = &absmax_stage1_kernel<G>;
+    return launch_k(k, chunk_grid<k>(nc, num_cus), s, x, n, nc, partial, amax);
+}
+
+template <int G>
+hipError_t launch_qg(const uint16_t *x, int64_t n, int64_t nc, uint8_t *codes, float *scales, float *partial,
+                     hipStream_t s, int num_cus) {
+    constexpr auto k = &quant_group_kernel<G>;
+    return launch_k(k, chunk_grid<k>(nc, num_cus), s, x, n, nc, codes, scales, partial);
+}
+
+hipError_t launch_stage2(const float *partial, int64_t n, float *amax, hipStream_t s, int num_cus) {
+    constexpr auto k = &absmax_stage2_kernel;
+    return launch_k(k, resident_grid<k>(ceil_div(n, (int64_t)kBlock * 4), num_cus), s, partial, n, amax);
+}
+
 }  // namespace
 
-hipError_t launch_absmax_reduce(const float *partial, int64_t n, float *amax, hipStream_t s, int grid_cap) {
+hipError_t launch_absmax_reduce(const float *partial, int64_t n, float *amax, hipStream_t s, int num_cus) {
     hipError_t e = launch_k(&zero_scalar_kernel, dim3(1), s, amax);
     if (e != hipSuccess) return e;
-    const int64_t blocks = ceil_div(n, (int64_t)kBlock * 4);
-    const dim3 grid((unsigned)(blocks < grid_cap ? (blocks > 0 ? blocks : 1) : grid_cap));
-    return launch_k(&absmax_stage2_kernel, grid, s, partial, n, amax);
+    return launch_stage2(partial, n, amax, s, num_cus);
 }
 
 hipError_t launch_group_absmax(const uint16_t *x, int64_t n, int G, float *partial, float *amax,
-                               hipStream_t s, int grid_cap) {
+                               hipStream_t s, int num_cus) {
     const int64_t nc = ceil_div(n, kWaveElems);
-    const dim3 grid = grid_for(nc, grid_cap);
     hipError_t e;
     switch (G) {
-    case 32: e = launch_k(&absmax_stage1_kernel<32>, grid, s, x, n, nc, partial, amax); break;
-    case 64: e = launch_k(&absmax_stage1_kernel<64>, grid, s, x, n, nc, partial, amax); break;
-    case 128: e = launch_k(&absmax_stage1_kernel<128>, grid, s, x, n, nc, partial, amax); break;
-    case 256: e = launch_k(&absmax_stage1_kernel<256>, grid, s, x, n, nc, partial, amax); break;
-    case 512: e = launch_k(&absmax_stage1_kernel<512>, grid, s, x, n, nc, partial, amax); break;
-    case 1024: e = launch_k(&absmax_stage1_kernel<1024>, grid, s, x, n, nc, partial, amax); break;
+    case 32: e = launch_stage1<32>(x, n, nc, partial, amax, s, num_cus); break;
+    case 64: e = launch_stage1<64>(x, n, nc, partial, amax, s, num_cus); break;
+    case 128: e = launch_stage1<128>(x, n, nc, partial, amax, s, num_cus); break;
+    case 256: e = launch_stage1<256>(x, n, nc, partial, amax, s, num_cus); break;
+    case 512: e = launch_stage1<512>(x, n, nc, partial, amax, s, num_cus); break;
+    case 1024: e = launch_stage1<1024>(x, n, nc, partial, amax, s, num_cus); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    const int64_t np = n / G;
-    const int64_t blocks = ceil_div(np, (int64_t)kBlock * 4);
-    const dim3 g2((unsigned)(blocks < grid_cap ? (blocks > 0 ? blocks : 1) : grid_cap));
-    return launch_k(&absmax_stage2_kernel, g2, s, (const float *)partial, np, amax);
+    return launch_stage2(partial, n / G, amax, s, num_cus);
 }
 
 hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *amax, uint8_t *codes,
-                                   float *scale, hipStream_t s, int grid_cap) {
+                                   float *scale, hipStream_t s, int num_cus) {
     const int64_t nc = ceil_div(n, kWaveElems);
-    return launch_k(&quant_per_tensor_kernel, grid_for(nc, grid_cap), s, x, n, nc, amax, codes, scale);
+    constexpr auto k = &quant_per_tensor_kernel;
+    return launch_k(k, chunk_grid<k>(nc, num_cus), s, x, n, nc, amax, codes, scale);
 }
 
 hipError_t launch_quant_group(const uint16_t *x, int64_t n, int G, uint8_t *codes, float *scales,
-                              float *partial, hipStream_t s, int grid_cap) {
+                              float *partial, hipStream_t s, int num_cus) {
     const int64_t nc = ceil_div(n, kWaveElems);
-    const dim3 grid = grid_for(nc, grid_cap);
     switch (G) {
-    case 32: return launch_k(&quant_group_kernel<32>, grid, s, x, n, nc, codes, scales, partial);
-    case 64: return launch_k(&quant_group_kernel<64>, grid, s, x, n, nc, codes, scales, partial);
-    case 128: return launch_k(&quant_group_kernel<128>, grid, s, x, n, nc, codes, scales, partial);
-    case 256: return launch_k(&quant_group_kernel<256>, grid, s, x, n, nc, codes, scales, partial);
-    case 512: return launch_k(&quant_group_kernel<512>, grid, s, x, n, nc, codes, scales, partial);
-    case 1024: return launch_k(&quant_group_kernel<1024>, grid, s, x, n, nc, codes, scales, partial);
+    case 32: return launch_qg<32>(x, n, nc, codes, scales, partial, s, num_cus);
+    case 64: return launch_qg<64>(x, n, nc, codes, scales, partial, s, num_cus);
+    case 128: return launch_qg<128>(x, n, nc, codes, scales, partial, s, num_cus);
+    case 256: return launch_qg<256>(x, n, nc, codes, scales, partial, s, num_cus);
+    case 512: return launch_qg<512>(x, n, nc, codes, scales, partial, s, num_cus);
+    case 1024: return launch_qg<1024>(x, n, nc, codes, scales, partial, s, num_cus);
     default: return hipErrorInvalidValue;
     }
 }

@@ -26,23 +26,58 @@ struct StepArgs {
     float decay;          // 1 - lr * weight_decay
     float m_log2_range;   // log2(MAX / smallest subnormal) of m's format
     float v_log2_range;   // ... of v's format
+    // log2(|decode(c)| / MAX) for every code magnitude c, as an FP32 hi + lo
+    // pair (code 0 and non-finite codes hold -2^100): m's format, then v's.
+    float2 log_tab[2][128];
 };
 
+// Fill tab[c] = log2(|decode(c)| / MAX) for the 128 code magnitudes of an OCP
+// FP8 format (0: E4M3, 1: E5M2), computed once per format in binary64.
+const float2 *fp8_log_table(int fmt);
+
+// Every launcher takes the device's compute-unit count.  Streaming kernels
+// give each wave one 1024-element chunk (no grid-stride loop: the hardware
+// dispatcher then sweeps the arrays in order, which keeps DRAM pages open);
+// the small reduction kernels are grid-stride with as many workgroups as can
+// be resident at once.
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
-                                 hipStream_t stream, int grid_cap);
+                                 hipStream_t stream, int num_cus);
 
 hipError_t launch_group_absmax(const uint16_t *x, int64_t n, int group_size, float *partial,
-                               float *amax, hipStream_t stream, int grid_cap);
+                               float *amax, hipStream_t stream, int num_cus);
 hipError_t launch_absmax_reduce(const float *partial, int64_t n, float *amax,
-                                hipStream_t stream, int grid_cap);
+                                hipStream_t stream, int num_cus);
 hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *amax,
-                                   uint8_t *codes, float *scale, hipStream_t stream, int grid_cap);
+                                   uint8_t *codes, float *scale, hipStream_t stream, int num_cus);
 hipError_t launch_quant_group(const uint16_t *x, int64_t n, int group_size, uint8_t *codes,
-                              float *scales, float *partial, hipStream_t stream, int grid_cap);
+                              float *scales, float *partial, hipStream_t stream, int num_cus);
 
 constexpr int kBlock = 256;       // threads per workgroup: 4 wave64s
 constexpr int kWaveElems = 1024;  // elements per wave pass: 64 lanes x 16
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups of `Kernel` resident on one CU (looked up once per kernel; the
+// answer depends only on the kernel's resources and the architecture).
+template <auto Kernel>
+inline int resident_blocks_per_cu() {
+    static int cached = 0;
+    const int v = __atomic_load_n(&cached, __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(Kernel), kBlock, 0) !=
+            hipSuccess || occ <= 0)
+        occ = 1;
+    __atomic_store_n(&cached, occ, __ATOMIC_RELAXED);
+    return occ;
+}
+
+// Grid for a grid-stride kernel needing `want` workgroups' worth of work.
+template <auto Kernel>
+inline dim3 resident_grid(int64_t want, int num_cus) {
+    const int64_t cap = (int64_t)resident_blocks_per_cu<Kernel>() * num_cus;
+    const int64_t g = want < cap ? want : cap;
+    return dim3((unsigned)(g > 0 ? g : 1));
+}
 
 }  // namespace coat

@@ -31,3 +31,23 @@ def golden_rows(name):
             if line and not line.startswith("#"):
                 rows.append(line.split())
     return rows
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the measured code-mismatch counts of the GPU parity tests next to
+    the other GPU run outputs (only when a GPU run produced some)."""
+    try:
+        import parity
+    except Exception:
+        return
+    if not parity.STATS:
+        return
+    import json
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    tot_n = sum(n for _, n, _ in parity.STATS)
+    tot_bad = sum(b for _, _, b in parity.STATS)
+    with open(os.path.join(out, "parity_code_stats.json"), "w") as f:
+        json.dump({"elements_compared": tot_n, "mismatching_codes": tot_bad,
+                   "mismatch_fraction": tot_bad / max(tot_n, 1),
+                   "per_comparison": [{"what": w, "n": n, "mismatches": b} for w, n, b in parity.STATS]}, f, indent=1)

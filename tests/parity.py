@@ -5,10 +5,12 @@ Tolerances (the product's contract with the oracle):
 * theta (FP32 master weights): |gpu - ref| <= 1e-6 |ref| + 1e-6 lr.  The
   absolute floor covers parameters that land near zero, where a relative
   bound is undefined; 1e-6 lr is a millionth of a typical update.
-* FP8 codes: identical (0x00 == 0x80) on >= 99.99% of each moment tensor and
-  every mismatch exactly one grid step -- the GPU evaluates the power with
-  FP32 exp2/log2 while the oracle uses binary64 pow, so an element within an
-  ulp or so of a rounding midpoint may land on the neighbouring code.
+* FP8 codes: identical (0x00 == 0x80) on >= 99.99% of each moment tensor
+  (at least one mismatch is allowed, so tensors under 10 000 elements may
+  hold a single one) and every mismatch exactly one grid step -- the GPU
+  evaluates the power with FP32 exp2/log2 while the oracle uses binary64 pow,
+  so an element within an ulp or so of a rounding midpoint may land on the
+  neighbouring code.
 * amax: within the FP32 rounding bound of the moment update, 2^-21 (2 amax_prev
   + amax) (a few ulps: the dequantized old moment carries the exp2 rounding).
 * k: within 1e-5 relative, plus the first-order effect on k of the FP32
@@ -34,6 +36,7 @@ LR, B1, B2, EPS, WD = (float(np.float32(v)) for v in
                        (inputs.LR, inputs.BETA1, inputs.BETA2, inputs.EPS, inputs.WEIGHT_DECAY))
 THREADS = 8
 CODE_MATCH_MIN = 0.9999
+STATS = []  # (what, elements, mismatching codes) of every code comparison, for the report
 
 
 def flush(msg: str):
@@ -98,7 +101,11 @@ def code_diff(gpu: np.ndarray, ref: np.ndarray):
 
 def assert_codes(gpu, ref, what, min_frac=CODE_MATCH_MIN):
     frac, steps = code_diff(gpu, ref)
-    assert frac >= min_frac, f"{what}: only {frac:.6%} codes identical"
+    n = gpu.size
+    bad = int(round((1.0 - frac) * n))
+    STATS.append((what, n, bad))
+    allowed = max(1, int((1.0 - min_frac) * n))
+    assert bad <= allowed, f"{what}: {bad} of {n} codes differ ({frac:.6%} identical)"
     assert steps <= 1, f"{what}: a code differs by {steps} grid steps"
     return frac
 
