@@ -12,6 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoat.so")
+CEILING_LIB = os.path.join(HERE, "libcoat_ceiling.so")  # memory-only reference kernels (benchmark only)
 ARCH = os.environ.get("COAT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -26,13 +27,18 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def _hipcc(out, srcs, verbose, extra=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", LIB + ".tmp", *sources()]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", out + ".tmp", *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    _hipcc(LIB, sources(), verbose, extra)
+    _hipcc(CEILING_LIB, sorted(glob.glob(os.path.join(CSRC, "ceiling", "*.hip"))), verbose, extra)
     return LIB
 
 

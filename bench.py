@@ -64,6 +64,45 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
+def memory_ceiling(theta, grad, st, n, alg_bytes, reps=3):
+    """What this device's HBM delivers for the step's own traffic: a memory-only
+    skeleton of the step (same bytes, same launch shape and lane layout, trivial
+    arithmetic) and a plain one-read-one-write copy, both from
+    libcoat_ceiling.so.  Run after the timed region, on the benchmark's own
+    buffers (it overwrites them)."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "activation_compression_amd", "libcoat_ceiling.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    L.coat_ceiling_step_skeleton.argtypes = [P] * 8 + [ctypes.c_int64, P]
+    L.coat_ceiling_copy.argtypes = [P, P, ctypes.c_int64, P]
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    ptrs = [P(t.data_ptr()) for t in (theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"],
+                                      st["v_amax"], st["v_k"])]
+
+    def timed(fn):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_skel = timed(lambda: L.coat_ceiling_step_skeleton(*ptrs, n, stream))
+    nbytes = grad.numel() * grad.element_size()
+    ms_copy = timed(lambda: L.coat_ceiling_copy(P(theta.data_ptr()), P(grad.data_ptr()), nbytes, stream))
+    return {"step_memory_skeleton_gb_per_s": round(alg_bytes / (ms_skel * 1e-3) / 1e9, 1),
+            "copy_gb_per_s": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(spec, acts, G, threads):
     """The oracle (as it stands) on a bounded sample of one step, scaled to
     params/s of the whole step.  Sample: the first two tensors of the arena
@@ -219,6 +258,9 @@ def main():
                     "frac_of_peak": round(alg[nm] / (per[nm] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)} for nm in names}
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
     traffic = measured_traffic()
+    ceiling = memory_ceiling(theta, grad, st, n, alg["adamw_fp8_step"])
+    if ceiling:
+        ceiling["frac_of_step_memory_skeleton"] = round(achieved / ceiling["step_memory_skeleton_gb_per_s"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,6 +293,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(alg["adamw_fp8_step"]),
+            "device_ceiling": ceiling,
         },
         "cpu_baseline": cpu,
         "kernels": kernels,

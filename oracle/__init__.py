@@ -56,7 +56,9 @@ def lib():
     L.orc_expand_quantize.argtypes = [i32, P, i64, f64, P, P, P]
     L.orc_expand_quantize.restype = None
     L.orc_expand_dequantize.argtypes, L.orc_expand_dequantize.restype = [i32, u32, f32, f32], f64
-    L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams)]
+    L.orc_expand_quantize_groups.argtypes = [i32, P, i64, i64, i64, P, P, P, P]
+    L.orc_expand_quantize_groups.restype = None
+    L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams), P, P]
     L.orc_adamw_step.restype = None
     L.orc_adamw_step_f64.argtypes = [P, P, P, P, i64, ctypes.POINTER(HParams)]
     L.orc_adamw_step_f64.restype = None
@@ -123,6 +125,26 @@ def expand_quantize(fmt, x, k_force: float = 0.0):
     return codes, np.float32(amax[0]), np.float32(k[0])
 
 
+def expand_quantize_groups(fmt, x, G: int, k_given=None, threads: int = 1):
+    """Quantize every G-element group of x; k_given (float32 per group) fixes
+    each group's k instead of recomputing it.  Returns (codes, amax, k)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    ng = x.size // G
+    codes = np.zeros(x.size, dtype=np.uint8)
+    amax = np.zeros(ng, dtype=np.float32)
+    k = np.zeros(ng, dtype=np.float32)
+    kg = None if k_given is None else np.ascontiguousarray(k_given, dtype=np.float32)
+    L = lib()
+    f = fmt_id(fmt)
+    ptrs = (_ptr(x), _ptr(kg) if kg is not None else None, _ptr(codes), _ptr(amax), _ptr(k))
+
+    def run(lo, hi):
+        L.orc_expand_quantize_groups(f, ptrs[0], lo, hi, G, ptrs[1], ptrs[2], ptrs[3], ptrs[4])
+
+    _run_blocks(run, _row_blocks(ng, threads), threads)
+    return codes, amax, k
+
+
 def expand_dequantize(fmt, codes, amax, k) -> np.ndarray:
     f = fmt_id(fmt)
     L = lib()
@@ -132,11 +154,13 @@ def expand_dequantize(fmt, codes, amax, k) -> np.ndarray:
 
 # ------------------------------------------------------------------ C4 AdamW
 def adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, *,
-               G: int, v_fmt, hp: HParams, groups=None, threads: int = 1) -> None:
+               G: int, v_fmt, hp: HParams, groups=None, threads: int = 1, moments_out=None) -> None:
     """One FP8-state AdamW step, in place on numpy arrays.
 
     ``groups`` = (g0, g1) restricts the step to a group range; ``threads``
     splits that range over host threads (the C code runs without the GIL).
+    ``moments_out`` = (m_new, v_new) float32 arrays like ``param`` receive the
+    new moments before requantization.
     """
     arrs = [param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k]
     for a in arrs:
@@ -146,11 +170,17 @@ def adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, *,
     n_groups = param.size // G
     g0, g1 = groups if groups is not None else (0, n_groups)
     ptrs = [_ptr(a) for a in arrs]
+    if moments_out is not None:
+        for a in moments_out:
+            assert a.dtype == np.float32 and a.size == param.size and a.flags["C_CONTIGUOUS"]
+        outs = [_ptr(a) for a in moments_out]
+    else:
+        outs = [None, None]
     L = lib()
     vf = fmt_id(v_fmt)
 
     def run(lo, hi):
-        L.orc_adamw_step(*ptrs, lo, hi, G, vf, ctypes.byref(hp))
+        L.orc_adamw_step(*ptrs, lo, hi, G, vf, ctypes.byref(hp), *outs)
 
     if threads <= 1 or g1 - g0 < 2 * threads:
         run(g0, g1)

@@ -216,6 +216,14 @@ void orc_expand_quantize(int fmt, const float *x, int64_t G, double k_force,
     *k_out = k;
 }
 
+void orc_expand_quantize_groups(int fmt, const float *x, int64_t g0, int64_t g1, int64_t G,
+                                const float *k_given, uint8_t *codes, float *amax, float *k)
+{
+    for (int64_t g = g0; g < g1; ++g)
+        orc_expand_quantize(fmt, x + g * G, G, k_given ? (double)k_given[g] : 0.0,
+                            codes + g * G, &amax[g], &k[g]);
+}
+
 /* [COAT] section "expansion function": dequantization applies the inverse
  * power 1/k to the decoded magnitude; the sign is carried by the code. */
 double orc_expand_dequantize(int fmt, uint32_t code, float amax, float k)
@@ -303,7 +311,7 @@ void orc_adamw_step(float *param, const uint16_t *grad,
                     uint8_t *m_codes, float *m_amax, float *m_k,
                     uint8_t *v_codes, float *v_amax, float *v_k,
                     int64_t g0, int64_t g1, int64_t G, int v_fmt,
-                    const orc_hparams *hp)
+                    const orc_hparams *hp, float *m_new_out, float *v_new_out)
 {
     float m_new[1024], v_new[1024];  /* G <= 1024 */
     adamw_consts c = adamw_setup(hp);
@@ -321,6 +329,8 @@ void orc_adamw_step(float *param, const uint16_t *grad,
             param[e] = (float)th;
             m_new[i] = (float)m1;
             v_new[i] = (float)v1;
+            if (m_new_out) m_new_out[e] = m_new[i];
+            if (v_new_out) v_new_out[e] = v_new[i];
         }
         orc_expand_quantize(ORC_E4M3, m_new, G, 0.0, m_codes + base, &m_amax[grp], &m_k[grp]);
         orc_expand_quantize(v_fmt, v_new, G, 0.0, v_codes + base, &v_amax[grp], &v_k[grp]);

@@ -65,6 +65,11 @@ uint32_t orc_fp8_max_code(int fmt);     /* code magnitude of the max value  */
 void orc_expand_quantize(int fmt, const float *x, int64_t G, double k_force,
                          uint8_t *codes, float *amax, float *k);
 
+/* orc_expand_quantize over groups [g0, g1) of x (G elements each); k_given
+ * (may be NULL) supplies each group's k instead of recomputing it. */
+void orc_expand_quantize_groups(int fmt, const float *x, int64_t g0, int64_t g1, int64_t G,
+                                const float *k_given, uint8_t *codes, float *amax, float *k);
+
 /* Inverse expansion of one code with its group's stored (amax, k). */
 double orc_expand_dequantize(int fmt, uint32_t code, float amax, float k);
 
@@ -77,12 +82,14 @@ typedef struct {
 
 /* One AdamW step over groups [g0, g1) of a flat parameter arena of G-element
  * groups.  m is E4M3; v is ORC_E4M3 or ORC_E5M2.  param, codes and per-group
- * (amax, k) are updated in place; grad holds BF16 bit patterns. */
+ * (amax, k) are updated in place; grad holds BF16 bit patterns.  m_new and
+ * v_new (each may be NULL) receive the new FP32 moments before they are
+ * requantized, indexed like param. */
 void orc_adamw_step(float *param, const uint16_t *grad,
                     uint8_t *m_codes, float *m_amax, float *m_k,
                     uint8_t *v_codes, float *v_amax, float *v_k,
                     int64_t g0, int64_t g1, int64_t G, int v_fmt,
-                    const orc_hparams *hp);
+                    const orc_hparams *hp, float *m_new, float *v_new);
 
 /* The same AdamW arithmetic with unquantized binary64 moments (used to pin
  * the update rule against an independent implementation). */

@@ -45,9 +45,11 @@ def pytest_sessionfinish(session, exitstatus):
     import json
     out = os.path.join(ROOT, "gpurun_out")
     os.makedirs(out, exist_ok=True)
-    tot_n = sum(n for _, n, _ in parity.STATS)
-    tot_bad = sum(b for _, _, b in parity.STATS)
+    tot_n = sum(r[1] for r in parity.STATS)
+    tot_bad = sum(r[2] for r in parity.STATS)
     with open(os.path.join(out, "parity_code_stats.json"), "w") as f:
         json.dump({"elements_compared": tot_n, "mismatching_codes": tot_bad,
                    "mismatch_fraction": tot_bad / max(tot_n, 1),
-                   "per_comparison": [{"what": w, "n": n, "mismatches": b} for w, n, b in parity.STATS]}, f, indent=1)
+                   "max_grid_steps": max(r[3] for r in parity.STATS),
+                   "per_comparison": [{"what": w, "n": n, "mismatches": b, "max_grid_steps": st}
+                                      for w, n, b, st in parity.STATS]}, f, indent=1)

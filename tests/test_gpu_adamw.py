@@ -162,3 +162,109 @@ def test_stress_64mi_launch_config_sampled():
     vc = st_g["v_codes"]
     assert (vc & 0x80 == 0).all() and ((vc & 0x7F) <= 0x7B).all()
     assert ((st_g["m_codes"] & 0x7F) != 0x7F).all()
+
+
+def _threads():
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _arena_step(th_d, g_d, st_d, spec, t):
+    coat.coat_adamw_step(th_d, g_d, st_d["m_codes"], st_d["m_amax"], st_d["m_k"], st_d["v_codes"],
+                         st_d["v_amax"], st_d["v_k"], group_size=spec.group_size, v_format=spec.v_fmt,
+                         hp=gpu_hp(t))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+def test_olmo1b_shaped_arena_two_steps_in_full():
+    """The whole OLMo-1B-shaped arena (1 176 764 416 params, v in E5M2) in one
+    launch, every element compared, two steps: step 2 starts from the
+    oracle's step-1 state copied onto the device."""
+    spec = inputs.olmo_1b()
+    G, n = spec.group_size, spec.numel
+    flush(f"generating {spec.name}")
+    th_d = inputs.gen_params(spec, device="cuda")
+    g1_d = inputs.gen_grads(spec, 1, device="cuda")
+    g2_d = inputs.gen_grads(spec, 2, device="cuda")
+    st_d = inputs.fresh_state(n, G, device="cuda")
+    theta0, g1, g2 = host(th_d), host(g1_d), host(g2_d)
+    st0 = np_state(n, G)
+    flush("GPU step 1")
+    _arena_step(th_d, g1_d, st_d, spec, 1)
+    gpu1 = (host(th_d), {k: host(v) for k, v in st_d.items()})
+    flush("oracle step 1")
+    ref1 = oracle_step(theta0, g1, st0, G, spec.v_fmt, 1, threads=_threads())
+    assert_step_parity(gpu1, ref1, spec.v_fmt, "olmo-1b step 1")
+    del gpu1
+    flush("GPU step 2 from the oracle's state")
+    th_d.copy_(torch.from_numpy(ref1[0]))
+    for k, v in ref1[1].items():
+        st_d[k].copy_(torch.from_numpy(v))
+    _arena_step(th_d, g2_d, st_d, spec, 2)
+    gpu2 = (host(th_d), {k: host(v) for k, v in st_d.items()})
+    flush("oracle step 2")
+    ref2 = oracle_step(ref1[0], g2, ref1[1], G, spec.v_fmt, 2, threads=_threads())
+    assert_step_parity(gpu2, ref2, spec.v_fmt, "olmo-1b step 2", prev=ref1[1])
+
+
+@pytest.mark.slow
+def test_olmo7b_shaped_arena_sampled():
+    """The benchmark's workload and launch configuration: the whole
+    OLMo-7B-shaped arena (6 888 095 744 params) in one launch.  Step 1 from a
+    fresh state is checked against its closed form on every element and
+    against the oracle on a seeded 1% sample of groups drawn across all
+    tensors; for step 2 the sampled groups are given the oracle's step-1 state
+    and compared again."""
+    spec = inputs.olmo_7b()
+    G, n = spec.group_size, spec.numel
+    ng = n // G
+    flush(f"generating {spec.name}")
+    th_d = inputs.gen_params(spec, device="cuda")
+    g1_d = inputs.gen_grads(spec, 1, device="cuda")
+    st_d = inputs.fresh_state(n, G, device="cuda")
+    rng = np.random.default_rng(7)
+    groups = np.sort(rng.choice(ng, ng // 100, replace=False))
+    gidx = torch.from_numpy(groups).cuda()
+    eidx = (gidx[:, None] * G + torch.arange(G, device="cuda")).reshape(-1)
+    theta0_s = host(th_d[eidx])
+    g1_s = host(g1_d[eidx])
+    theta0_d = th_d.clone()
+    flush("GPU step 1 (full arena)")
+    _arena_step(th_d, g1_d, st_d, spec, 1)
+
+    # closed form over every element, in float64 chunks on the device
+    decay = 1.0 - LR * float(np.float32(inputs.WEIGHT_DECAY))
+    eps = float(np.float32(inputs.EPS))
+    worst = 0.0
+    for c0 in range(0, n, 1 << 28):
+        c1 = min(n, c0 + (1 << 28))
+        g = (g1_d[c0:c1].to(torch.int32) << 16).view(torch.float32).double()
+        want = theta0_d[c0:c1].double() * decay - LR * g / (g.abs() + eps)
+        err = (th_d[c0:c1].double() - want).abs() - (1e-6 * want.abs() + 1e-6 * LR)
+        worst = max(worst, err.max().item())
+    assert worst <= 0.0, f"closed form violated by {worst:.3e}"
+    del theta0_d
+
+    def sample(st):
+        return {"m_codes": host(st["m_codes"][eidx]), "v_codes": host(st["v_codes"][eidx]),
+                "m_amax": host(st["m_amax"][gidx]), "m_k": host(st["m_k"][gidx]),
+                "v_amax": host(st["v_amax"][gidx]), "v_k": host(st["v_k"][gidx])}
+
+    flush(f"oracle step 1 on {groups.size} groups")
+    st0 = np_state(eidx.numel(), G)
+    ref1 = oracle_step(theta0_s, g1_s, st0, G, spec.v_fmt, 1, threads=_threads())
+    assert_step_parity((host(th_d[eidx]), sample(st_d)), ref1, spec.v_fmt, "olmo-7b step 1 sampled")
+
+    flush("GPU step 2 with the oracle's state in the sampled groups")
+    g2_d = inputs.gen_grads(spec, 2, device="cuda", out=g1_d)
+    g2_s = host(g2_d[eidx])
+    th_d[eidx] = torch.from_numpy(ref1[0]).cuda()
+    for k in ("m_codes", "v_codes"):
+        st_d[k][eidx] = torch.from_numpy(ref1[1][k]).cuda()
+    for k in ("m_amax", "m_k", "v_amax", "v_k"):
+        st_d[k][gidx] = torch.from_numpy(ref1[1][k]).cuda()
+    _arena_step(th_d, g2_d, st_d, spec, 2)
+    flush("oracle step 2")
+    ref2 = oracle_step(ref1[0], g2_s, ref1[1], G, spec.v_fmt, 2, threads=_threads())
+    assert_step_parity((host(th_d[eidx]), sample(st_d)), ref2, spec.v_fmt, "olmo-7b step 2 sampled", prev=ref1[1])
