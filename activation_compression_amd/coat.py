@@ -48,8 +48,13 @@ def lib():
     L.coat_absmax_reduce.argtypes = [P, i64, P, P]
     L.coat_quant_per_tensor.argtypes = [P, i64, P, P, P, P]
     L.coat_quant_group.argtypes = [P, i64, i64, i32, P, P, P, P]
+    L.coat_adamw_step_bf16.argtypes = [P, P, P, P, P, P, P, P, P, i64, i32, ctypes.c_int,
+                                       ctypes.POINTER(AdamWHParams), P]
+    L.coat_dequant_per_tensor.argtypes = [P, i64, P, P, P]
+    L.coat_dequant_group.argtypes = [P, i64, i64, i32, P, P, P]
     for f in (L.coat_adamw_step, L.coat_group_absmax, L.coat_absmax_reduce,
-              L.coat_quant_per_tensor, L.coat_quant_group):
+              L.coat_quant_per_tensor, L.coat_quant_group, L.coat_adamw_step_bf16,
+              L.coat_dequant_per_tensor, L.coat_dequant_group):
         f.restype = ctypes.c_int
     L.coat_status_string.argtypes = [ctypes.c_int]
     L.coat_status_string.restype = ctypes.c_char_p
@@ -109,6 +114,20 @@ def coat_adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k
            "coat_adamw_step")
 
 
+def coat_adamw_step_bf16(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, param_bf16, *,
+                         group_size: int = 128, v_format="e4m3", hp: AdamWHParams, n: int | None = None,
+                         stream=None) -> None:
+    """coat_adamw_step that also writes the BF16 working copy of the new weights."""
+    n = param.numel() if n is None else int(n)
+    ng = n // group_size if group_size > 0 else 0
+    args = [_ptr(param, _F32, "param", n), _ptr(grad_bf16, _U16, "grad_bf16", n),
+            _ptr(m_codes, _U8, "m_codes", n), _ptr(m_amax, _F32, "m_amax", ng), _ptr(m_k, _F32, "m_k", ng),
+            _ptr(v_codes, _U8, "v_codes", n), _ptr(v_amax, _F32, "v_amax", ng), _ptr(v_k, _F32, "v_k", ng),
+            _ptr(param_bf16, _U16, "param_bf16", n)]
+    _check(lib().coat_adamw_step_bf16(*args, n, group_size, _FMT[v_format], ctypes.byref(hp), _stream(stream)),
+           "coat_adamw_step_bf16")
+
+
 def coat_group_absmax(x_bf16, partial_amax, amax, *, group_size: int = 128, stream=None) -> None:
     """Two-stage Group Scaling absmax of a 2-D BF16 tensor."""
     rows, cols = x_bf16.shape
@@ -139,3 +158,19 @@ def coat_quant_group(x_bf16, codes, scales, partial_amax=None, *, group_size: in
                                   _ptr(codes, _U8, "codes", rows * cols), _ptr(scales, _F32, "scales", ng),
                                   _ptr(partial_amax, _F32, "partial_amax", ng), _stream(stream)),
            "coat_quant_group")
+
+
+def coat_dequant_per_tensor(codes, scale, out_bf16, *, stream=None) -> None:
+    """E4M3 codes times the per-tensor scale, to BF16."""
+    n = codes.numel()
+    _check(lib().coat_dequant_per_tensor(_ptr(codes, _U8, "codes"), n, _ptr(scale, _F32, "scale", 1),
+                                         _ptr(out_bf16, _U16, "out_bf16", n), _stream(stream)),
+           "coat_dequant_per_tensor")
+
+
+def coat_dequant_group(codes, scales, out_bf16, *, rows: int, cols: int, group_size: int = 128, stream=None) -> None:
+    """1xG E4M3 codes times their slice scales, to BF16."""
+    ng = rows * (cols // group_size)
+    _check(lib().coat_dequant_group(_ptr(codes, _U8, "codes", rows * cols), rows, cols, group_size,
+                                    _ptr(scales, _F32, "scales", ng), _ptr(out_bf16, _U16, "out_bf16", rows * cols),
+                                    _stream(stream)), "coat_dequant_group")

@@ -54,14 +54,19 @@ const char *coat_status_string(coat_status s) {
     return "unknown status";
 }
 
-coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax,
-                            float *m_k, uint8_t *v_codes, float *v_amax, float *v_k, int64_t n,
-                            int32_t group_size, coat_fp8_format v_format, const coat_adamw_hparams *hp,
+}  // extern "C"
+
+namespace {
+
+coat_status adamw_step_impl(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax, float *m_k,
+                            uint8_t *v_codes, float *v_amax, float *v_k, int64_t n, int32_t group_size,
+                            coat_fp8_format v_format, const coat_adamw_hparams *hp, uint16_t *param_bf16,
                             void *stream) {
     if (!param || !grad_bf16 || !m_codes || !m_amax || !m_k || !v_codes || !v_amax || !v_k || !hp)
         return COAT_ERR_NULL;
     if (!aligned(param, 16) || !aligned(grad_bf16, 16) || !aligned(m_codes, 16) || !aligned(v_codes, 16) ||
-        !aligned(m_amax, 4) || !aligned(m_k, 4) || !aligned(v_amax, 4) || !aligned(v_k, 4))
+        !aligned(m_amax, 4) || !aligned(m_k, 4) || !aligned(v_amax, 4) || !aligned(v_k, 4) ||
+        (param_bf16 && !aligned(param_bf16, 16)))
         return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
     if (n <= 0 || n % group_size != 0) return COAT_ERR_SHAPE;
@@ -91,7 +96,29 @@ coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16, uint8_t *m_
     a.v_log2_range = v_format == COAT_FP8_E5M2 ? (float)(log2(57344.0) + 16.0) : a.m_log2_range;
     memcpy(a.log_tab[0], coat::fp8_log_table(COAT_FP8_E4M3), sizeof a.log_tab[0]);
     memcpy(a.log_tab[1], coat::fp8_log_table((int)v_format), sizeof a.log_tab[1]);
+    a.param_bf16 = param_bf16;
     return from_hip(coat::launch_adamw_fp8_step(a, group_size, (int)v_format, (hipStream_t)stream, num_cus()));
+}
+
+}  // namespace
+
+extern "C" {
+
+coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax,
+                            float *m_k, uint8_t *v_codes, float *v_amax, float *v_k, int64_t n,
+                            int32_t group_size, coat_fp8_format v_format, const coat_adamw_hparams *hp,
+                            void *stream) {
+    return adamw_step_impl(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, n, group_size, v_format,
+                           hp, nullptr, stream);
+}
+
+coat_status coat_adamw_step_bf16(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax,
+                                 float *m_k, uint8_t *v_codes, float *v_amax, float *v_k, uint16_t *param_bf16,
+                                 int64_t n, int32_t group_size, coat_fp8_format v_format,
+                                 const coat_adamw_hparams *hp, void *stream) {
+    if (!param_bf16) return COAT_ERR_NULL;
+    return adamw_step_impl(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, n, group_size, v_format,
+                           hp, param_bf16, stream);
 }
 
 coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t group_size,
@@ -131,6 +158,24 @@ coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
     if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_quant_group(x_bf16, rows * cols, group_size, codes, scales,
                                              partial_amax_or_null, (hipStream_t)stream, num_cus()));
+}
+
+coat_status coat_dequant_per_tensor(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out_bf16,
+                                    void *stream) {
+    if (!codes || !scale || !out_bf16) return COAT_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scale, 4)) return COAT_ERR_ALIGN;
+    if (n <= 0 || n % 8 != 0) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_dequant_per_tensor(codes, n, scale, out_bf16, (hipStream_t)stream));
+}
+
+coat_status coat_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int32_t group_size,
+                               const float *scales, uint16_t *out_bf16, void *stream) {
+    if (!codes || !scales || !out_bf16) return COAT_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales, 4)) return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_dequant_group(codes, rows * cols, group_size, scales, out_bf16,
+                                               (hipStream_t)stream));
 }
 
 }  // extern "C"

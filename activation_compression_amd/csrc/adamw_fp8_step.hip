@@ -134,7 +134,7 @@ __device__ __forceinline__ float expand(float xs, float amq, float invq, float k
 // One wave's pass over 1024 consecutive parameters starting at `base` (wave-
 // uniform).  kTail: the last, partial chunk -- lanes past n load nothing and
 // store nothing (their whole groups are past n as well, since n % G == 0).
-template <int G, int VF, bool kTail>
+template <int G, int VF, bool kTail, bool kBf16>
 __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab, int64_t base, int lane) {
     constexpr int LPG = G / 16;  // lanes per group (2 .. 64)
     const int j = lane & (LPG - 1);
@@ -213,6 +213,13 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             pp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
+        if constexpr (kBf16) {  // the working copy the next forward pass reads
+            uint4 *bp = reinterpret_cast<uint4 *>(a.param_bf16 + base) + lane * 2;
+            bp[0] = make_uint4(bf16x2(th[0], th[1]), bf16x2(th[2], th[3]), bf16x2(th[4], th[5]),
+                               bf16x2(th[6], th[7]));
+            bp[1] = make_uint4(bf16x2(th[8], th[9]), bf16x2(th[10], th[11]), bf16x2(th[12], th[13]),
+                               bf16x2(th[14], th[15]));
+        }
     }
 
     // group statistics (non-negative floats order like their bit patterns)
@@ -270,7 +277,7 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
     }
 }
 
-template <int G, int VF>
+template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a) {
     // Per code byte (both signs): [0, 256) m codes (E4M3), [256, 512) v codes.
     __shared__ float2 tab[512];
@@ -286,28 +293,28 @@ __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (chunk >= a.n_chunks) return;
     if (chunk < a.n / kWaveElems)  // every lane in range
-        step_chunk<G, VF, false>(a, tab, chunk * kWaveElems, lane);
+        step_chunk<G, VF, false, kBf16>(a, tab, chunk * kWaveElems, lane);
     else
-        step_chunk<G, VF, true>(a, tab, chunk * kWaveElems, lane);
+        step_chunk<G, VF, true, kBf16>(a, tab, chunk * kWaveElems, lane);
 }
 
-template <int G, int VF>
+template <int G, int VF, bool kBf16>
 hipError_t launch(const StepArgs &a, hipStream_t stream, int num_cus) {
-    constexpr auto kernel = &adamw_fp8_step_kernel<G, VF>;
+    constexpr auto kernel = &adamw_fp8_step_kernel<G, VF, kBf16>;
     const dim3 grid((unsigned)ceil_div(a.n_chunks, kBlock / 64));
     void *args[] = {const_cast<StepArgs *>(&a)};
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
 }
 
-template <int VF>
+template <int VF, bool kBf16>
 hipError_t launch_g(const StepArgs &a, int G, hipStream_t s, int cap) {
     switch (G) {
-    case 32: return launch<32, VF>(a, s, cap);
-    case 64: return launch<64, VF>(a, s, cap);
-    case 128: return launch<128, VF>(a, s, cap);
-    case 256: return launch<256, VF>(a, s, cap);
-    case 512: return launch<512, VF>(a, s, cap);
-    case 1024: return launch<1024, VF>(a, s, cap);
+    case 32: return launch<32, VF, kBf16>(a, s, cap);
+    case 64: return launch<64, VF, kBf16>(a, s, cap);
+    case 128: return launch<128, VF, kBf16>(a, s, cap);
+    case 256: return launch<256, VF, kBf16>(a, s, cap);
+    case 512: return launch<512, VF, kBf16>(a, s, cap);
+    case 1024: return launch<1024, VF, kBf16>(a, s, cap);
     default: return hipErrorInvalidValue;
     }
 }
@@ -344,8 +351,11 @@ const float2 *fp8_log_table(int fmt) {
 
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
                                  hipStream_t stream, int num_cus) {
-    return v_format == kE5M2 ? launch_g<kE5M2>(a, group_size, stream, num_cus)
-                             : launch_g<kE4M3>(a, group_size, stream, num_cus);
+    if (a.param_bf16)
+        return v_format == kE5M2 ? launch_g<kE5M2, true>(a, group_size, stream, num_cus)
+                                 : launch_g<kE4M3, true>(a, group_size, stream, num_cus);
+    return v_format == kE5M2 ? launch_g<kE5M2, false>(a, group_size, stream, num_cus)
+                             : launch_g<kE4M3, false>(a, group_size, stream, num_cus);
 }
 
 }  // namespace coat

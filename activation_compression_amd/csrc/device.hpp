@@ -52,6 +52,20 @@ __device__ __forceinline__ float decode1(uint32_t c) {
         return __builtin_amdgcn_cvt_f32_bf8((int)c, 0);
 }
 
+// Two FP32 values to a packed pair of BF16 (round to nearest even, native
+// v_cvt_pk_bf16_f32): a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const v2f v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// Decode E4M3 code bytes 0,1 (kHi = false) or 2,3 (kHi = true) of w to FP32.
+template <bool kHi>
+__device__ __forceinline__ v2f decode2_e4m3(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+}
+
 // ---- bit helpers
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -29,6 +29,7 @@ struct StepArgs {
     // log2(|decode(c)| / MAX) for every code magnitude c, as an FP32 hi + lo
     // pair (code 0 and non-finite codes hold -2^100): m's format, then v's.
     float2 log_tab[2][128];
+    uint16_t *param_bf16;  // BF16 working copy of the updated weights, or null
 };
 
 // Fill tab[c] = log2(|decode(c)| / MAX) for the 128 code magnitudes of an OCP
@@ -51,6 +52,10 @@ hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *am
                                    uint8_t *codes, float *scale, hipStream_t stream, int num_cus);
 hipError_t launch_quant_group(const uint16_t *x, int64_t n, int group_size, uint8_t *codes,
                               float *scales, float *partial, hipStream_t stream, int num_cus);
+hipError_t launch_dequant_per_tensor(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
+                                     hipStream_t stream);
+hipError_t launch_dequant_group(const uint8_t *codes, int64_t n, int group_size, const float *scales,
+                                uint16_t *out, hipStream_t stream);
 
 constexpr int kBlock = 256;       // threads per workgroup: 4 wave64s
 constexpr int kWaveElems = 1024;  // elements per wave pass: 64 lanes x 16

@@ -107,6 +107,24 @@ coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16,
                             const coat_adamw_hparams *hp, void *stream);
 
 /*
+ * coat_adamw_step_bf16 -- coat_adamw_step that also writes the BF16 working
+ * copy of the updated master weights, round to nearest even, from the same
+ * pass ([LPF]: FP32 master weights are updated, the BF16 copy is what the
+ * forward and backward passes compute with).  2 extra bytes per parameter
+ * instead of a separate cast kernel's 6.
+ *
+ * param_bf16  BF16 bit patterns [n], written.  16-byte aligned; must not
+ *             overlap any other argument.  All other arguments, layout and
+ *             errors as coat_adamw_step (NULL param_bf16 -> COAT_ERR_NULL).
+ */
+coat_status coat_adamw_step_bf16(float *param, const uint16_t *grad_bf16,
+                                 uint8_t *m_codes, float *m_amax, float *m_k,
+                                 uint8_t *v_codes, float *v_amax, float *v_k,
+                                 uint16_t *param_bf16,
+                                 int64_t n, int32_t group_size, coat_fp8_format v_format,
+                                 const coat_adamw_hparams *hp, void *stream);
+
+/*
  * coat_group_absmax -- both stages of Group Scaling ([COAT] section "mixed
  * granularity"): stage 1 writes the max |x| of every 1xG slice of each row,
  * stage 2 reduces that G-times-smaller tensor to the tensor absmax.
@@ -163,6 +181,26 @@ coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float
 coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
                              int32_t group_size, uint8_t *codes, float *scales,
                              float *partial_amax_or_null, void *stream);
+
+/*
+ * coat_dequant_per_tensor / coat_dequant_group -- E4M3 activations back to
+ * BF16 for the backward pass, the consumer half of activation compression
+ * ([COAT] sections "why activations are hard" and "mixed granularity":
+ * compressed activations are saved for, and read back in, the backward pass).
+ * Per element: y = FP32(decode(code) * scale) (the correctly rounded FP32
+ * product), stored as BF16, round to nearest even.
+ *
+ * codes     E4M3 [n] or [rows x cols], read only.  16-byte aligned.
+ * scale     FP32 [1] device scalar (per-tensor), as written by
+ *           coat_quant_per_tensor.  4-byte aligned.
+ * scales    FP32 [rows * cols / G] (group), as written by coat_quant_group.
+ * out_bf16  BF16 bit patterns, same count as codes, written.  16-byte aligned.
+ * n         > 0, a multiple of 8.  rows, cols, G as for coat_quant_group.
+ */
+coat_status coat_dequant_per_tensor(const uint8_t *codes, int64_t n, const float *scale,
+                                    uint16_t *out_bf16, void *stream);
+coat_status coat_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int32_t group_size,
+                               const float *scales, uint16_t *out_bf16, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *coat_status_string(coat_status s);

@@ -58,6 +58,15 @@ def lib():
     L.orc_expand_dequantize.argtypes, L.orc_expand_dequantize.restype = [i32, u32, f32, f32], f64
     L.orc_expand_quantize_groups.argtypes = [i32, P, i64, i64, i64, P, P, P, P]
     L.orc_expand_quantize_groups.restype = None
+    L.orc_expand_dequantize_groups.argtypes = [i32, P, i64, i64, i64, P, P, P]
+    L.orc_expand_dequantize_groups.restype = None
+    L.orc_bf16_rne.argtypes, L.orc_bf16_rne.restype = [f32], ctypes.c_uint16
+    L.orc_adamw_step_bf16.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams), P]
+    L.orc_adamw_step_bf16.restype = None
+    L.orc_dequant_per_tensor.argtypes = [P, i64, f32, P]
+    L.orc_dequant_per_tensor.restype = None
+    L.orc_dequant_group.argtypes = [P, i64, i64, i64, P, P]
+    L.orc_dequant_group.restype = None
     L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams), P, P]
     L.orc_adamw_step.restype = None
     L.orc_adamw_step_f64.argtypes = [P, P, P, P, i64, ctypes.POINTER(HParams)]
@@ -145,6 +154,28 @@ def expand_quantize_groups(fmt, x, G: int, k_given=None, threads: int = 1):
     return codes, amax, k
 
 
+def expand_dequantize_groups(fmt, codes, G: int, amax, k, threads: int = 1) -> np.ndarray:
+    """Inverse expansion of every code (binary64 values)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    kk = np.ascontiguousarray(k, dtype=np.float32)
+    out = np.zeros(c.size, dtype=np.float64)
+    L = lib()
+    f = fmt_id(fmt)
+
+    def run(lo, hi):
+        L.orc_expand_dequantize_groups(f, _ptr(c), lo, hi, G, _ptr(a), _ptr(kk), _ptr(out))
+
+    _run_blocks(run, _row_blocks(c.size // G, threads), threads)
+    return out
+
+
+def bf16_rne(x) -> np.ndarray:
+    """BF16 bit patterns (uint16) of FP32 values, round to nearest even."""
+    L = lib()
+    return np.array([L.orc_bf16_rne(float(v)) for v in np.asarray(x, dtype=np.float32).ravel()], dtype=np.uint16)
+
+
 def expand_dequantize(fmt, codes, amax, k) -> np.ndarray:
     f = fmt_id(fmt)
     L = lib()
@@ -188,6 +219,24 @@ def adamw_step(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, *,
     bounds = np.linspace(g0, g1, threads + 1).astype(np.int64)
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda i: run(int(bounds[i]), int(bounds[i + 1])), range(threads)))
+
+
+def adamw_step_bf16(param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, param_bf16, *,
+                    G: int, v_fmt, hp: HParams, threads: int = 1) -> None:
+    """adamw_step that also writes the BF16 working copy of the new weights."""
+    arrs = [param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, param_bf16]
+    for a in arrs:
+        assert a.flags["C_CONTIGUOUS"]
+    assert param_bf16.dtype == np.uint16 and param_bf16.size == param.size
+    ptrs = [_ptr(a) for a in arrs]
+    L = lib()
+    vf = fmt_id(v_fmt)
+    ng = param.size // G
+
+    def run(lo, hi):
+        L.orc_adamw_step_bf16(*ptrs[:8], lo, hi, G, vf, ctypes.byref(hp), ptrs[8])
+
+    _run_blocks(run, _row_blocks(ng, threads), threads)
 
 
 def adamw_step_f64(param, grad, m, v, hp: HParams) -> None:
@@ -265,3 +314,32 @@ def quant_group(x_bf16, G: int, threads: int = 1):
 
     _run_blocks(run, _row_blocks(rows, threads), threads)
     return codes, scales, partial
+
+
+# ------------------------------------------------ activation dequantization
+def dequant_per_tensor(codes, scale, threads: int = 1) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    out = np.zeros(c.size, dtype=np.uint16)
+    L = lib()
+    bounds = [(lo * 16, min(c.size, hi * 16)) for lo, hi in _row_blocks((c.size + 15) // 16, threads)]
+
+    def run(lo, hi):
+        L.orc_dequant_per_tensor(_ptr(c[lo:hi]), hi - lo, float(scale), _ptr(out[lo:hi]))
+
+    _run_blocks(run, bounds, threads)
+    return out
+
+
+def dequant_group(codes, rows: int, cols: int, G: int, scales, threads: int = 1) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(rows, cols)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    gpr = cols // G
+    out = np.zeros(rows * cols, dtype=np.uint16)
+    L = lib()
+
+    def run(lo, hi):
+        L.orc_dequant_group(_ptr(c[lo:hi]), hi - lo, cols, G, _ptr(sc[lo * gpr:hi * gpr]),
+                            _ptr(out[lo * cols:hi * cols]))
+
+    _run_blocks(run, _row_blocks(rows, threads), threads)
+    return out

@@ -235,6 +235,52 @@ double orc_expand_dequantize(int fmt, uint32_t code, float amax, float k)
     return d < 0 ? -mag : mag;
 }
 
+void orc_expand_dequantize_groups(int fmt, const uint8_t *codes, int64_t g0, int64_t g1, int64_t G,
+                                  const float *amax, const float *k, double *out)
+{
+    for (int64_t g = g0; g < g1; ++g)
+        for (int64_t i = 0; i < G; ++i)
+            out[g * G + i] = orc_expand_dequantize(fmt, codes[g * G + i], amax[g], k[g]);
+}
+
+/* ======================================================================== */
+/* BF16 rounding                                                             */
+/* ======================================================================== */
+
+/*
+ * BF16 keeps FP32's sign and 8-bit exponent and 7 explicit mantissa bits
+ * ([LPF]; [ATLAS] "01 Number anatomy"), i.e. an 8-bit significand.  Round to
+ * nearest, ties to even, by scaling the significand to an integer: frexp
+ * gives x = f 2^e with 0.5 <= |f| < 1, so f * 2^8 carries the 8 kept bits in
+ * its integer part, and rint (round-half-even in the default rounding mode)
+ * rounds the rest away.  Values below the smallest normal keep the normal
+ * exponent floor (BF16 subnormals have the same spacing as FP32's exponent
+ * floor allows: 2^-133).  The result is exact in binary64 and representable
+ * in FP32, so its bit pattern's top half is the BF16 code.
+ */
+uint16_t orc_bf16_rne(float xf)
+{
+    double x = (double)xf;
+    union { float f; uint32_t u; } cv;
+    if (x == 0.0 || isnan(x) || isinf(x)) {
+        cv.f = xf;
+        return (uint16_t)(cv.u >> 16);
+    }
+    int e;
+    double f = frexp(x, &e);               /* x = f * 2^e */
+    if (e < -125) {                        /* below the normal range: fixed spacing 2^-133 */
+        f = ldexp(x, 133);
+        e = 0;
+        cv.f = (float)ldexp(rint(f), -133);
+        return (uint16_t)(cv.u >> 16);
+    }
+    double r = ldexp(rint(ldexp(f, 8)), e - 8);
+    if (fabs(r) > 3.3895313892515355e38)   /* rounds past the largest BF16 value */
+        r = x > 0 ? INFINITY : -INFINITY;
+    cv.f = (float)r;
+    return (uint16_t)(cv.u >> 16);
+}
+
 /* ======================================================================== */
 /* C4. AdamW with FP8 moments                                                */
 /* ======================================================================== */
@@ -337,6 +383,20 @@ void orc_adamw_step(float *param, const uint16_t *grad,
     }
 }
 
+/* The working copy the forward/backward pass computes with ([LPF]: FP32
+ * master weights, BF16 for the matrix products) taken right after the update. */
+void orc_adamw_step_bf16(float *param, const uint16_t *grad,
+                         uint8_t *m_codes, float *m_amax, float *m_k,
+                         uint8_t *v_codes, float *v_amax, float *v_k,
+                         int64_t g0, int64_t g1, int64_t G, int v_fmt,
+                         const orc_hparams *hp, uint16_t *param_bf16)
+{
+    orc_adamw_step(param, grad, m_codes, m_amax, m_k, v_codes, v_amax, v_k, g0, g1, G, v_fmt, hp,
+                   NULL, NULL);
+    for (int64_t e = g0 * G; e < g1 * G; ++e)
+        param_bf16[e] = orc_bf16_rne(param[e]);
+}
+
 /* ======================================================================== */
 /* C5. Group Scaling and activation quantization                             */
 /* ======================================================================== */
@@ -422,4 +482,35 @@ void orc_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
                 codes[base + i] = scaled_e4m3(bf16_to_double(x_bf16[base + i]), a);
             scales[r * gpr + j] = (float)(a / 448.0);
         }
+}
+
+/*
+ * The consumer half of activation compression ([COAT] "mixed granularity"
+ * and "why activations are hard": compressed activations are saved for the
+ * backward pass and read back there): decode the E4M3 code, multiply by the
+ * stored scale in FP32 (the product of a 4-bit and a 24-bit significand is
+ * exact in binary64, then rounded once to FP32), round to BF16.
+ */
+static uint16_t dequant_one(uint8_t code, float scale)
+{
+    float y = (float)(orc_fp8_decode(ORC_E4M3, code) * (double)scale);
+    return orc_bf16_rne(y);
+}
+
+void orc_dequant_per_tensor(const uint8_t *codes, int64_t n, float scale, uint16_t *out_bf16)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out_bf16[i] = dequant_one(codes[i], scale);
+}
+
+void orc_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int64_t G,
+                       const float *scales, uint16_t *out_bf16)
+{
+    int64_t gpr = cols / G;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < gpr; ++j)
+            for (int64_t i = 0; i < G; ++i) {
+                int64_t e = r * cols + j * G + i;
+                out_bf16[e] = dequant_one(codes[e], scales[r * gpr + j]);
+            }
 }

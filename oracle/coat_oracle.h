@@ -73,6 +73,13 @@ void orc_expand_quantize_groups(int fmt, const float *x, int64_t g0, int64_t g1,
 /* Inverse expansion of one code with its group's stored (amax, k). */
 double orc_expand_dequantize(int fmt, uint32_t code, float amax, float k);
 
+/* orc_expand_dequantize of every code of groups [g0, g1) (G codes each). */
+void orc_expand_dequantize_groups(int fmt, const uint8_t *codes, int64_t g0, int64_t g1, int64_t G,
+                                  const float *amax, const float *k, double *out);
+
+/* Round-to-nearest-even of an FP32 value to BF16, returned as its bit pattern. */
+uint16_t orc_bf16_rne(float x);
+
 /* ---- C4: AdamW step with FP8 first/second moments ----------------------- */
 
 typedef struct {
@@ -90,6 +97,14 @@ void orc_adamw_step(float *param, const uint16_t *grad,
                     uint8_t *v_codes, float *v_amax, float *v_k,
                     int64_t g0, int64_t g1, int64_t G, int v_fmt,
                     const orc_hparams *hp, float *m_new, float *v_new);
+
+/* The same step, also writing the BF16 working copy of the updated FP32
+ * master weights (round to nearest even) to param_bf16 (indexed like param). */
+void orc_adamw_step_bf16(float *param, const uint16_t *grad,
+                         uint8_t *m_codes, float *m_amax, float *m_k,
+                         uint8_t *v_codes, float *v_amax, float *v_k,
+                         int64_t g0, int64_t g1, int64_t G, int v_fmt,
+                         const orc_hparams *hp, uint16_t *param_bf16);
 
 /* The same AdamW arithmetic with unquantized binary64 moments (used to pin
  * the update rule against an independent implementation). */
@@ -116,6 +131,13 @@ void orc_quant_per_tensor(const uint16_t *x_bf16, int64_t n, float amax,
  * be NULL) receives a. */
 void orc_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
                      int64_t G, uint8_t *codes, float *scales, float *partial);
+
+/* Dequantization of E4M3 activations for the backward pass: per element the
+ * FP32 product decode(code) * scale, rounded to BF16 (nearest even).
+ * Per-tensor: one scale; group: scales[r*(cols/G)+j] for slice j of row r. */
+void orc_dequant_per_tensor(const uint8_t *codes, int64_t n, float scale, uint16_t *out_bf16);
+void orc_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int64_t G,
+                       const float *scales, uint16_t *out_bf16);
 
 #ifdef __cplusplus
 }

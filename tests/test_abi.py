@@ -28,8 +28,9 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for want in ("coat_adamw_step", "coat_group_absmax", "coat_absmax_reduce",
-                 "coat_quant_per_tensor", "coat_quant_group", "coat_status_string"):
+    for want in ("coat_adamw_step", "coat_adamw_step_bf16", "coat_group_absmax", "coat_absmax_reduce",
+                 "coat_quant_per_tensor", "coat_quant_group", "coat_dequant_per_tensor",
+                 "coat_dequant_group", "coat_status_string"):
         assert want in names
 
 
@@ -104,3 +105,18 @@ def test_activation_entry_points_validate(L):
     assert L.coat_quant_group(f, 4, 256, 128, f, f, P(FAKE + 2), None) == 2
     assert L.coat_quant_group(f, 4, 256, 64 * 3, f, f, None, None) == 4
     assert L.coat_quant_group(f, 4, 96, 32, P(0), f, None, None) == 1
+
+
+def test_new_entry_points_validate(L):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    ptrs = [f] * 8
+    assert L.coat_adamw_step_bf16(*ptrs, P(0), 1024, 128, 0, ctypes.byref(hp()), None) == 1
+    assert L.coat_adamw_step_bf16(*ptrs, P(FAKE + 8), 1024, 128, 0, ctypes.byref(hp()), None) == 2
+    assert L.coat_adamw_step_bf16(*ptrs, f, 1000, 128, 0, ctypes.byref(hp()), None) == 3
+    assert L.coat_dequant_per_tensor(f, 12, f, f, None) == 3
+    assert L.coat_dequant_per_tensor(P(FAKE + 4), 16, f, f, None) == 2
+    assert L.coat_dequant_per_tensor(f, 16, P(0), f, None) == 1
+    assert L.coat_dequant_group(f, 4, 256, 100, f, f, None) == 4
+    assert L.coat_dequant_group(f, 4, 200, 128, f, f, None) == 3
+    assert L.coat_dequant_group(f, 4, 256, 128, f, P(FAKE + 2), None) == 2

@@ -162,3 +162,43 @@ def test_group_cast_full_size(which):
     rc, rs, rp = orc.quant_group(host(x), 128, threads=THREADS)
     assert (host(scales) == rs).all() and (host(partial) == rp).all()
     assert (norm0(host(codes)) == rc).all()
+
+
+def random_codes_and_scales(rows, cols, G, seed):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, rows * cols).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    scales = (np.abs(rng.standard_normal(rows * cols // G)) * 10.0 ** rng.uniform(-6, 3, rows * cols // G)).astype(np.float32)
+    return codes, scales
+
+
+@pytest.mark.parametrize("G", [32, 128, 1024])
+def test_dequant_group_small(G):
+    codes, scales = random_codes_and_scales(48, 2048, G, seed=G)
+    out = torch.empty(codes.size, dtype=torch.int16, device="cuda")
+    coat.coat_dequant_group(dev(codes), dev(scales), out, rows=48, cols=2048, group_size=G)
+    torch.cuda.synchronize()
+    assert (host(out) == orc.dequant_group(codes, 48, 2048, G, scales)).all()
+
+
+@pytest.mark.parametrize("n", [4096 * 8, 1032 * 5])
+def test_dequant_per_tensor_small(n):
+    codes, scales = random_codes_and_scales(1, n, 8, seed=n)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    coat.coat_dequant_per_tensor(dev(codes), dev(scales[:1]), out)
+    torch.cuda.synchronize()
+    assert (host(out) == orc.dequant_per_tensor(codes, scales[0])).all()
+
+
+@pytest.mark.slow
+def test_quant_dequant_roundtrip_full_size():
+    """[16384 x 11008]: the oracle's 1x128 quantization of the SwiGLU input,
+    dequantized on the GPU, bit-exact against the oracle's dequantization."""
+    spec = inputs.swiglu_input()
+    x = inputs.gen_activation(spec).numpy().view(np.uint16)
+    codes, scales, _ = orc.quant_group(x, 128, threads=THREADS)
+    out = torch.empty(spec.numel, dtype=torch.int16, device="cuda")
+    flush("dequant 16384x11008")
+    coat.coat_dequant_group(dev(codes), dev(scales), out, rows=spec.rows, cols=spec.cols, group_size=128)
+    torch.cuda.synchronize()
+    assert (host(out) == orc.dequant_group(codes, spec.rows, spec.cols, 128, scales, threads=THREADS)).all()

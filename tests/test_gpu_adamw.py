@@ -8,7 +8,7 @@ import torch
 
 import oracle as orc
 from activation_compression_amd import coat, inputs
-from parity import (LR, assert_codes, assert_step_parity, assert_theta, dev, flush, gpu_hp, gpu_step,
+from parity import (LR, assert_codes, assert_step_parity, assert_theta, dev, flush, gpu_hp, gpu_step, orc_hp,
                     host, np_state, oracle_step)
 
 pytestmark = [pytest.mark.gpu,
@@ -268,3 +268,36 @@ def test_olmo7b_shaped_arena_sampled():
     flush("oracle step 2")
     ref2 = oracle_step(ref1[0], g2_s, ref1[1], G, spec.v_fmt, 2, threads=_threads())
     assert_step_parity((host(th_d[eidx]), sample(st_d)), ref2, spec.v_fmt, "olmo-7b step 2 sampled", prev=ref1[1])
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_step_with_bf16_working_copy(v_fmt):
+    """coat_adamw_step_bf16: the same update as coat_adamw_step (identical
+    bytes), plus the BF16 copy of the new weights -- round to nearest even of
+    the GPU's own FP32 result (checked with torch's cast) and within one BF16
+    step of the oracle's copy."""
+    spec, theta, (g1, g2) = config1_inputs(2)
+    G = 128
+    st0 = np_state(spec.numel, G)
+    ref1 = oracle_step(theta, g1, st0, G, v_fmt, 1)
+    for t, g, th_in, st_in in ((1, g1, theta, st0), (2, g2, ref1[0], ref1[1])):
+        plain = gpu_step(th_in, g, st_in, G, v_fmt, t)
+        th = dev(th_in)
+        s = {k: dev(v) for k, v in st_in.items()}
+        copy = torch.empty(spec.numel, dtype=torch.int16, device="cuda")
+        coat.coat_adamw_step_bf16(th, dev(g), s["m_codes"], s["m_amax"], s["m_k"], s["v_codes"], s["v_amax"],
+                                  s["v_k"], copy, group_size=G, v_format=v_fmt, hp=gpu_hp(t))
+        torch.cuda.synchronize()
+        assert (host(th) == plain[0]).all() and all((host(s[k]) == plain[1][k]).all() for k in s)
+        assert (copy == th.to(torch.bfloat16).view(torch.int16)).all().item()
+        ref_copy = np.zeros(spec.numel, np.uint16)
+        st_r = {k: v.copy() for k, v in st_in.items()}
+        th_r = th_in.copy()
+        orc.adamw_step_bf16(th_r, g, st_r["m_codes"], st_r["m_amax"], st_r["m_k"], st_r["v_codes"], st_r["v_amax"],
+                            st_r["v_k"], ref_copy, G=G, v_fmt=v_fmt, hp=orc_hp(t), threads=8)
+        # values: within theta's tolerance plus one BF16 step of the oracle's copy
+        got = (host(copy).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        want = (ref_copy.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        tol = 1e-6 * np.abs(th_r.astype(np.float64)) + 1e-6 * LR + np.spacing(np.abs(want).astype(np.float32)) * 2 ** 16
+        assert (np.abs(got - want) <= tol).all()
+        assert (got == want).mean() > 0.9999
