@@ -52,6 +52,8 @@ def lib():
                                        ctypes.POINTER(AdamWHParams), P]
     L.coat_dequant_per_tensor.argtypes = [P, i64, P, P, P]
     L.coat_dequant_group.argtypes = [P, i64, i64, i32, P, P, P]
+    L.coat_swiglu_fused.argtypes = [P, P, i64, i64, i32, P, P, P, P, P, P, P]
+    L.coat_swiglu_fused.restype = ctypes.c_int
     for f in (L.coat_adamw_step, L.coat_group_absmax, L.coat_absmax_reduce,
               L.coat_quant_per_tensor, L.coat_quant_group, L.coat_adamw_step_bf16,
               L.coat_dequant_per_tensor, L.coat_dequant_group):
@@ -174,3 +176,22 @@ def coat_dequant_group(codes, scales, out_bf16, *, rows: int, cols: int, group_s
     _check(lib().coat_dequant_group(_ptr(codes, _U8, "codes", rows * cols), rows, cols, group_size,
                                     _ptr(scales, _F32, "scales", ng), _ptr(out_bf16, _U16, "out_bf16", rows * cols),
                                     _stream(stream)), "coat_dequant_group")
+
+
+def coat_swiglu_fused(gate_bf16, up_bf16, h_bf16, h_partial, saved=None, *, group_size: int = 128,
+                      stream=None) -> None:
+    """h = silu(gate) * up (BF16) with the per-1xG maxima of h (Group Scaling
+    stage 1); saved = (gate_codes, gate_scales, up_codes, up_scales) also
+    stores the inputs in 1xG E4M3 for the backward pass."""
+    rows, cols = gate_bf16.shape
+    n, ng = rows * cols, rows * (cols // group_size)
+    if saved is None:
+        sv = [None, None, None, None]
+    else:
+        gc, gs, uc, us = saved
+        sv = [_ptr(gc, _U8, "gate_codes", n), _ptr(gs, _F32, "gate_scales", ng),
+              _ptr(uc, _U8, "up_codes", n), _ptr(us, _F32, "up_scales", ng)]
+    _check(lib().coat_swiglu_fused(_ptr(gate_bf16, _U16, "gate_bf16", n), _ptr(up_bf16, _U16, "up_bf16", n),
+                                   rows, cols, group_size, _ptr(h_bf16, _U16, "h_bf16", n),
+                                   _ptr(h_partial, _F32, "h_partial", ng), *sv, _stream(stream)),
+           "coat_swiglu_fused")

@@ -178,4 +178,20 @@ coat_status coat_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols,
                                                (hipStream_t)stream));
 }
 
+coat_status coat_swiglu_fused(const uint16_t *gate_bf16, const uint16_t *up_bf16, int64_t rows, int64_t cols,
+                              int32_t group_size, uint16_t *h_bf16, float *h_partial_amax, uint8_t *gate_codes,
+                              float *gate_scales, uint8_t *up_codes, float *up_scales, void *stream) {
+    if (!gate_bf16 || !up_bf16 || !h_bf16 || !h_partial_amax) return COAT_ERR_NULL;
+    const int saved = !!gate_codes + !!gate_scales + !!up_codes + !!up_scales;
+    if (saved != 0 && saved != 4) return COAT_ERR_NULL;
+    if (!aligned(gate_bf16, 16) || !aligned(up_bf16, 16) || !aligned(h_bf16, 16) || !aligned(h_partial_amax, 4) ||
+        (saved && (!aligned(gate_codes, 16) || !aligned(up_codes, 16) || !aligned(gate_scales, 4) ||
+                   !aligned(up_scales, 4))))
+        return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    return from_hip(coat::launch_swiglu_fused(gate_bf16, up_bf16, rows * cols, group_size, h_bf16, h_partial_amax,
+                                              gate_codes, gate_scales, up_codes, up_scales, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -54,6 +54,9 @@ hipError_t launch_quant_group(const uint16_t *x, int64_t n, int group_size, uint
                               float *scales, float *partial, hipStream_t stream, int num_cus);
 hipError_t launch_dequant_per_tensor(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
                                      hipStream_t stream);
+hipError_t launch_swiglu_fused(const uint16_t *gate, const uint16_t *up, int64_t n, int group_size, uint16_t *h,
+                               float *h_partial, uint8_t *gate_codes, float *gate_scales, uint8_t *up_codes,
+                               float *up_scales, hipStream_t stream);
 hipError_t launch_dequant_group(const uint8_t *codes, int64_t n, int group_size, const float *scales,
                                 uint16_t *out, hipStream_t stream);
 

@@ -187,6 +187,16 @@ def swiglu_input(rows: int = 16384, cols: int = 11008) -> ActivationSpec:
     return ActivationSpec(f"swiglu-in-{rows}x{cols}", rows, cols, seed=2001)
 
 
+def swiglu_gate(rows: int = 16384, cols: int = 11008) -> ActivationSpec:
+    """Gate projection output feeding SwiGLU, [16384 tokens x 11008]."""
+    return ActivationSpec(f"swiglu-gate-{rows}x{cols}", rows, cols, seed=2002)
+
+
+def swiglu_up(rows: int = 16384, cols: int = 11008) -> ActivationSpec:
+    """Up projection output feeding SwiGLU, [16384 tokens x 11008]."""
+    return ActivationSpec(f"swiglu-up-{rows}x{cols}", rows, cols, seed=2003)
+
+
 def outlier_channels(spec: ActivationSpec) -> torch.Tensor:
     g = _gen(spec.seed + 1, "cpu")
     return torch.randperm(spec.cols, generator=g)[: spec.n_outlier_channels]

@@ -202,6 +202,33 @@ coat_status coat_dequant_per_tensor(const uint8_t *codes, int64_t n, const float
 coat_status coat_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int32_t group_size,
                                const float *scales, uint16_t *out_bf16, void *stream);
 
+/*
+ * coat_swiglu_fused -- SwiGLU with Group Scaling stage 1 fused into its
+ * epilogue ([COAT] "mixed granularity": the per-slice max is cached by the op
+ * that produces the tensor, so stage 1 costs no second read; [COAT] "why
+ * activations are hard": GLU-type activations are the outlier-heavy ones).
+ *   h = silu(gate) * up, silu(x) = x / (1 + e^-x), in FP32, stored as BF16
+ *   (round to nearest even); h_partial_amax[r*(cols/G)+j] = max |h| over
+ *   slice j of row r (as stored).  coat_absmax_reduce then gives the tensor
+ *   absmax for coat_quant_per_tensor of h (the down projection's input).
+ * Optionally, in the same pass, SwiGLU's own inputs are saved for the
+ * backward pass as 1xG E4M3 exactly as coat_quant_group would write them.
+ *
+ * gate_bf16, up_bf16  BF16 [rows x cols] row-major, read only.  16-byte aligned.
+ * h_bf16              BF16 [rows x cols], written.  16-byte aligned.
+ * h_partial_amax      FP32 [rows * cols / G], written.  4-byte aligned.
+ * gate_codes, up_codes    E4M3 [rows x cols] or NULL; 16-byte aligned.
+ * gate_scales, up_scales  FP32 [rows * cols / G] or NULL; all four NULL or
+ *                     all four set (else COAT_ERR_NULL).
+ * rows, cols, G as for coat_quant_group.  h agrees with a binary64 evaluation
+ * rounded to FP32 and then BF16 to within one BF16 step (FP32 exp and
+ * reciprocal).
+ */
+coat_status coat_swiglu_fused(const uint16_t *gate_bf16, const uint16_t *up_bf16, int64_t rows, int64_t cols,
+                              int32_t group_size, uint16_t *h_bf16, float *h_partial_amax,
+                              uint8_t *gate_codes, float *gate_scales, uint8_t *up_codes, float *up_scales,
+                              void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *coat_status_string(coat_status s);
 

@@ -67,6 +67,9 @@ def lib():
     L.orc_dequant_per_tensor.restype = None
     L.orc_dequant_group.argtypes = [P, i64, i64, i64, P, P]
     L.orc_dequant_group.restype = None
+    L.orc_silu.argtypes, L.orc_silu.restype = [f64], f64
+    L.orc_swiglu_absmax.argtypes = [P, P, i64, i64, i64, P, P]
+    L.orc_swiglu_absmax.restype = None
     L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams), P, P]
     L.orc_adamw_step.restype = None
     L.orc_adamw_step_f64.argtypes = [P, P, P, P, i64, ctypes.POINTER(HParams)]
@@ -343,3 +346,26 @@ def dequant_group(codes, rows: int, cols: int, G: int, scales, threads: int = 1)
 
     _run_blocks(run, _row_blocks(rows, threads), threads)
     return out
+
+
+# ------------------------------------------- SwiGLU producer with stage 1
+def silu(x: float) -> float:
+    return lib().orc_silu(float(x))
+
+
+def swiglu_absmax(gate_bf16, up_bf16, G: int, threads: int = 1):
+    """(h BF16 bits [rows*cols], partial absmax of h per 1xG slice)."""
+    g = np.ascontiguousarray(gate_bf16, dtype=np.uint16)
+    u = np.ascontiguousarray(up_bf16, dtype=np.uint16)
+    rows, cols = g.shape
+    gpr = cols // G
+    h = np.zeros(rows * cols, dtype=np.uint16)
+    partial = np.zeros(rows * gpr, dtype=np.float32)
+    L = lib()
+
+    def run(lo, hi):
+        L.orc_swiglu_absmax(_ptr(g[lo:hi]), _ptr(u[lo:hi]), hi - lo, cols, G, _ptr(h[lo * cols:hi * cols]),
+                            _ptr(partial[lo * gpr:hi * gpr]))
+
+    _run_blocks(run, _row_blocks(rows, threads), threads)
+    return h, partial

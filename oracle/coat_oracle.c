@@ -514,3 +514,35 @@ void orc_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int64_t
                 out_bf16[e] = dequant_one(codes[e], scales[r * gpr + j]);
             }
 }
+
+/* ======================================================================== */
+/* SwiGLU producer with Group Scaling stage 1 in its epilogue                */
+/* ======================================================================== */
+
+/* The GLU-type activation of [COAT] "why activations are hard": SiLU of the
+ * gate times the up projection.  Its output is a linear layer's input, whose
+ * per-tensor scale needs the Group Scaling absmax; [COAT] "mixed granularity"
+ * has stage 1 fused into the op that produces the tensor. */
+double orc_silu(double x)
+{
+    return x / (1.0 + exp(-x));
+}
+
+void orc_swiglu_absmax(const uint16_t *gate, const uint16_t *up, int64_t rows, int64_t cols, int64_t G,
+                       uint16_t *h_bf16, float *partial)
+{
+    int64_t gpr = cols / G;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < gpr; ++j) {
+            double mx = 0.0;
+            for (int64_t i = 0; i < G; ++i) {
+                int64_t e = r * cols + j * G + i;
+                double h = orc_silu(bf16_to_double(gate[e])) * bf16_to_double(up[e]);
+                uint16_t b = orc_bf16_rne((float)h);
+                h_bf16[e] = b;
+                double a = fabs(bf16_to_double(b));
+                if (a > mx) mx = a;
+            }
+            partial[r * gpr + j] = (float)mx;
+        }
+}

@@ -139,6 +139,14 @@ void orc_dequant_per_tensor(const uint8_t *codes, int64_t n, float scale, uint16
 void orc_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols, int64_t G,
                        const float *scales, uint16_t *out_bf16);
 
+/* SwiGLU with Group Scaling stage 1 fused into its epilogue: per element
+ * h = silu(gate) * up (silu(x) = x / (1 + e^-x)), formed in binary64, rounded
+ * to FP32 and then to BF16 (nearest even); partial[r*(cols/G)+j] = max |h| over
+ * slice j of row r (h as stored). */
+double orc_silu(double x);
+void orc_swiglu_absmax(const uint16_t *gate, const uint16_t *up, int64_t rows, int64_t cols, int64_t G,
+                       uint16_t *h_bf16, float *partial);
+
 #ifdef __cplusplus
 }
 #endif

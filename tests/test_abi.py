@@ -30,7 +30,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for want in ("coat_adamw_step", "coat_adamw_step_bf16", "coat_group_absmax", "coat_absmax_reduce",
                  "coat_quant_per_tensor", "coat_quant_group", "coat_dequant_per_tensor",
-                 "coat_dequant_group", "coat_status_string"):
+                 "coat_dequant_group", "coat_swiglu_fused", "coat_status_string"):
         assert want in names
 
 
@@ -120,3 +120,13 @@ def test_new_entry_points_validate(L):
     assert L.coat_dequant_group(f, 4, 256, 100, f, f, None) == 4
     assert L.coat_dequant_group(f, 4, 200, 128, f, f, None) == 3
     assert L.coat_dequant_group(f, 4, 256, 128, f, P(FAKE + 2), None) == 2
+
+
+def test_swiglu_validates(L):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    assert L.coat_swiglu_fused(P(0), f, 4, 256, 128, f, f, None, None, None, None, None) == 1
+    assert L.coat_swiglu_fused(f, f, 4, 256, 128, f, f, f, None, None, None, None) == 1  # partial save set
+    assert L.coat_swiglu_fused(f, P(FAKE + 2), 4, 256, 128, f, f, None, None, None, None, None) == 2
+    assert L.coat_swiglu_fused(f, f, 4, 200, 128, f, f, None, None, None, None, None) == 3
+    assert L.coat_swiglu_fused(f, f, 4, 256, 96, f, f, None, None, None, None, None) == 4

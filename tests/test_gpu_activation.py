@@ -202,3 +202,113 @@ def test_quant_dequant_roundtrip_full_size():
     coat.coat_dequant_group(dev(codes), dev(scales), out, rows=spec.rows, cols=spec.cols, group_size=128)
     torch.cuda.synchronize()
     assert (host(out) == orc.dequant_group(codes, spec.rows, spec.cols, 128, scales, threads=THREADS)).all()
+
+
+# ---------------------------------------------------------- fused SwiGLU (f1)
+def bf16_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_step(x):
+    """One BF16 step (ulp) at |x|: 2^(e-7) for normal x, the subnormal step below."""
+    ax = np.abs(np.asarray(x, np.float32))
+    e = np.floor(np.log2(np.maximum(ax, np.float32(2.0 ** -126))))
+    return np.exp2(e - 7).astype(np.float32)
+
+
+# silu(g) is flushed to -0 by the kernel once e^-g leaves the FP32 range
+# (g < -87.3); there |silu(g)| < 1.6e-36, so |h| < 1.6e-36 |up|.
+FLUSH_GATE = -87.0
+
+
+def assert_h_close(h_gpu, h_ref, gate, up, what):
+    """h in value space within one BF16 step of the oracle's (the kernel's FP32
+    silu is a few FP32 ulps off, which moves a BF16 rounding by one step at
+    most), at least 99.9% identical; flushed tails as documented above."""
+    hg, hr = bf16_f32(h_gpu), bf16_f32(h_ref)
+    g, u = bf16_f32(gate).reshape(-1), bf16_f32(up).reshape(-1)
+    flushed = (g < FLUSH_GATE) & (hg == 0)
+    assert (np.abs(hr[flushed]) <= 1.6e-36 * np.abs(u[flushed])).all(), what
+    ok = flushed | (np.abs(hg - hr) <= bf16_step(hr))
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond one BF16 step"
+    same = (h_gpu == h_ref) | flushed
+    frac = np.count_nonzero(same) / same.size
+    assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
+    return frac
+
+
+def gpu_swiglu(gate, up, G, save):
+    rows, cols = gate.shape
+    n, ng = rows * cols, rows * cols // G
+    h = torch.empty(n, dtype=torch.int16, device="cuda")
+    hp = torch.empty(ng, device="cuda")
+    saved = None
+    if save:
+        saved = (torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(ng, device="cuda"),
+                 torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(ng, device="cuda"))
+    gd, ud = (dev(gate), dev(up)) if isinstance(gate, np.ndarray) else (gate, up)
+    coat.coat_swiglu_fused(gd, ud, h, hp, saved, group_size=G)
+    torch.cuda.synchronize()
+    return host(h), host(hp), None if saved is None else [host(t) for t in saved]
+
+
+def check_swiglu(gate, up, G, h, hp, saved, what, threads=1):
+    h_ref, p_ref = orc.swiglu_absmax(gate, up, G, threads=threads)
+    frac = assert_h_close(h, h_ref, gate, up, what)
+    # stage 1 is the exact slice max of h as the kernel stored it ...
+    own = np.abs(bf16_f32(h)).reshape(-1, G).max(axis=1)
+    assert (hp == own).all(), what
+    # ... and within one BF16 step of the oracle's
+    assert (np.abs(hp - p_ref) <= bf16_step(p_ref)).all(), what
+    if saved is not None:
+        gc, gs, uc, us = saved
+        rgc, rgs, _ = orc.quant_group(gate, G, threads=threads)
+        ruc, rus, _ = orc.quant_group(up, G, threads=threads)
+        assert (norm0(gc) == rgc).all() and (gs == rgs).all(), what
+        assert (norm0(uc) == ruc).all() and (us == rus).all(), what
+    return frac
+
+
+@pytest.mark.parametrize("G", [32, 128, 1024])
+@pytest.mark.parametrize("save", [False, True])
+def test_swiglu_fused_small(G, save):
+    gate, up = act(40, 2048, seed=100 + G), act(40, 2048, seed=200 + G)
+    gate[3, :G] = 0          # silu(0) = 0: an all-zero slice of h and of gate
+    up[4, G:2 * G] = 0x8000  # -0 up
+    gate[7, :16] = np.array([0xC2B4, 0xC2C8, 0xC300, 0x42C8, 0x4700, 0xC700, 0x3F80, 0xBF80] * 2,
+                            np.uint16)  # -90, -100, -128, 100, +-32768, +-1
+    flush(f"swiglu G={G} save={save}")
+    h, hp, saved = gpu_swiglu(gate, up, G, save)
+    check_swiglu(gate, up, G, h, hp, saved, f"G={G}")
+
+
+def test_swiglu_fused_ragged():
+    """rows * cols not a multiple of the 1024-element wave chunk."""
+    gate, up = act(3, 96, seed=11), act(3, 96, seed=12)
+    h, hp, saved = gpu_swiglu(gate, up, 32, True)
+    check_swiglu(gate, up, 32, h, hp, saved, "3x96")
+
+
+def test_swiglu_then_per_tensor_cast():
+    """The fused stage 1 feeds stage 2 and the per-tensor cast of h, exactly as
+    an unfused coat_group_absmax of the same h would."""
+    gate, up = act(64, 4096, seed=21), act(64, 4096, seed=22)
+    h, hp, _ = gpu_swiglu(gate, up, 128, False)
+    amax = torch.empty(1, device="cuda")
+    coat.coat_absmax_reduce(dev(hp), amax)
+    partial2, amax2 = gpu_group_absmax(h.reshape(64, 4096), 128)
+    torch.cuda.synchronize()
+    assert (partial2 == hp).all() and host(amax)[0] == amax2
+
+
+@pytest.mark.slow
+def test_swiglu_fused_full_size():
+    """[16384 x 11008] gate and up with x100 outlier channels, inputs saved, in
+    the launch configuration timed."""
+    gs, us = inputs.swiglu_gate(), inputs.swiglu_up()
+    gate = inputs.gen_activation(gs).numpy().view(np.uint16)
+    up = inputs.gen_activation(us).numpy().view(np.uint16)
+    flush(f"fused swiglu on {gs.name}")
+    h, hp, saved = gpu_swiglu(gate, up, 128, True)
+    frac = check_swiglu(gate, up, 128, h, hp, saved, "16384x11008", threads=THREADS)
+    flush(f"h identical fraction {frac:.7f}")
