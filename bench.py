@@ -15,7 +15,12 @@ the dominant kernel, the AdamW step: algorithmic bytes per launch
 HIP events on the stream it runs on.  The CPU baseline is the oracle on a
 bounded sample of the same step, on the host's cores.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Beside the step (not in `value`), "extras" times the other entry points on
+the same resident workloads: the step with its BF16 working copy, the fused
+SwiGLU producer with Group Scaling stage 1 in its epilogue, and the FP8 ->
+BF16 activation dequantization.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
 """
 import argparse
 import hashlib
@@ -103,6 +108,83 @@ def memory_ceiling(theta, grad, st, n, alg_bytes, reps=3):
             "copy_gb_per_s": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1)}
 
 
+def time_launches(fn, reps):
+    """Average milliseconds of `fn` (launches on torch's current stream), HIP
+    events on that stream around `reps` back-to-back calls after one warm-up."""
+    import torch
+
+    fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def entry(alg_bytes, ms, elems=None):
+    d = {"ms": round(ms, 4), "algorithmic_bytes": int(alg_bytes),
+         "gb_per_s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+         "frac_of_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if elems:
+        d["elements_per_s"] = elems / (ms * 1e-3)
+    return d
+
+
+def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
+    """The entry points beside the timed step, each timed alone on the same
+    HBM-resident workloads: the step with its BF16 working-copy output; the
+    fused SwiGLU producer (stage 1 in its epilogue, with and without saving
+    its inputs in 1xG E4M3), against SwiGLU followed by a separate stage-1
+    pass over h; and the FP8 -> BF16 dequantization of saved activations."""
+    import torch
+
+    out = {}
+    n = spec.numel
+    f = float
+    hp = lambda t: coat.adamw_hparams(f(inputs.LR), f(inputs.BETA1), f(inputs.BETA2), f(inputs.EPS),
+                                      f(inputs.WEIGHT_DECAY), t)
+    wcopy = torch.empty(n, dtype=torch.int16, device="cuda")
+    ms = time_launches(lambda i: coat.coat_adamw_step_bf16(
+        theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"], st["v_k"], wcopy,
+        group_size=G, v_format=spec.v_fmt, hp=hp(step0 + i)), 3)
+    out["adamw_fp8_step_bf16_copy"] = entry(n * (16.0 + 32.0 / G), ms, n)
+    del wcopy
+
+    gs, us = inputs.swiglu_gate(), inputs.swiglu_up()
+    N = gs.numel
+    gate, up = inputs.gen_activation(gs, device="cuda"), inputs.gen_activation(us, device="cuda")
+    h = torch.empty(N, dtype=torch.int16, device="cuda")
+    hp_ = torch.empty(N // G, device="cuda")
+    saved = (torch.empty(N, dtype=torch.uint8, device="cuda"), torch.empty(N // G, device="cuda"),
+             torch.empty(N, dtype=torch.uint8, device="cuda"), torch.empty(N // G, device="cuda"))
+    amax = torch.empty(1, device="cuda")
+    ms_f = time_launches(lambda i: coat.coat_swiglu_fused(gate, up, h, hp_, None, group_size=G), reps)
+    ms_s = time_launches(lambda i: coat.coat_swiglu_fused(gate, up, h, hp_, saved, group_size=G), reps)
+    h2 = h.view(gs.rows, gs.cols)
+    ms_a = time_launches(lambda i: coat.coat_group_absmax(h2, hp_, amax, group_size=G), reps)
+    shape = f"{gs.rows}x{gs.cols}"
+    out[f"swiglu_fused_{shape}"] = entry(6 * N + 4 * N / G, ms_f, N)
+    out[f"swiglu_fused_save_inputs_{shape}"] = entry(8 * N + 12 * N / G, ms_s, N)
+    out[f"swiglu_then_separate_stage1_{shape}"] = {
+        "ms": round(ms_f + ms_a, 4), "algorithmic_bytes": int(8 * N + 8 * N / G),
+        "stage1_share_fused": round(4 * N / G / (6 * N + 4 * N / G), 4),
+        "stage1_share_separate": round(ms_a / (ms_f + ms_a), 4)}
+
+    codes, scales = saved[0], saved[1]
+    out16 = h
+    ms_dg = time_launches(lambda i: coat.coat_dequant_group(codes, scales, out16, rows=gs.rows, cols=gs.cols,
+                                                              group_size=G), reps)
+    out[f"dequant_group_{shape}"] = entry(3 * N + 4 * N / G, ms_dg, N)
+    ms_dt = time_launches(lambda i: coat.coat_dequant_per_tensor(codes, scales[:1], out16), reps)
+    out[f"dequant_per_tensor_{shape}"] = entry(3 * N + 4, ms_dt, N)
+    del gate, up, h, hp_, saved
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(spec, acts, G, threads):
     """The oracle (as it stands) on a bounded sample of one step, scaled to
     params/s of the whole step.  Sample: the first two tensors of the arena
@@ -162,6 +244,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the entry points timed beside the step")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of a known size (to scale the HBM byte counters)")
@@ -258,6 +341,7 @@ def main():
                     "frac_of_peak": round(alg[nm] / (per[nm] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)} for nm in names}
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
     traffic = measured_traffic()
+    extra = None if args.no_extras else extras(coat, inputs, theta, grad, st, spec, G, step + 1)
     ceiling = memory_ceiling(theta, grad, st, n, alg["adamw_fp8_step"])
     if ceiling:
         ceiling["frac_of_step_memory_skeleton"] = round(achieved / ceiling["step_memory_skeleton_gb_per_s"], 4)
@@ -297,6 +381,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "extras": extra,
         "step_hbm_gb_per_s": round(sum(alg.values()) / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
     }

@@ -70,6 +70,8 @@ def lib():
     L.orc_silu.argtypes, L.orc_silu.restype = [f64], f64
     L.orc_swiglu_absmax.argtypes = [P, P, i64, i64, i64, P, P]
     L.orc_swiglu_absmax.restype = None
+    L.orc_rmsnorm_absmax.argtypes = [P, P, i64, i64, i64, ctypes.c_float, P, P, P]
+    L.orc_rmsnorm_absmax.restype = None
     L.orc_adamw_step.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, ctypes.POINTER(HParams), P, P]
     L.orc_adamw_step.restype = None
     L.orc_adamw_step_f64.argtypes = [P, P, P, P, i64, ctypes.POINTER(HParams)]
@@ -369,3 +371,25 @@ def swiglu_absmax(gate_bf16, up_bf16, G: int, threads: int = 1):
 
     _run_blocks(run, _row_blocks(rows, threads), threads)
     return h, partial
+
+
+# ------------------------------------------ RMSNorm producer with stage 1
+def rmsnorm_absmax(x_bf16, weight_bf16, G: int, eps: float, threads: int = 1):
+    """(y BF16 bits [rows*cols], partial absmax of y per 1xG slice, rstd FP32 [rows]);
+    weight_bf16 may be None (no gain)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    w = None if weight_bf16 is None else np.ascontiguousarray(weight_bf16, dtype=np.uint16).reshape(-1)
+    assert w is None or w.size == cols
+    gpr = cols // G
+    y = np.zeros(rows * cols, dtype=np.uint16)
+    partial = np.zeros(rows * gpr, dtype=np.float32)
+    rstd = np.zeros(rows, dtype=np.float32)
+    L = lib()
+
+    def run(lo, hi):
+        L.orc_rmsnorm_absmax(_ptr(x[lo:hi]), None if w is None else _ptr(w), hi - lo, cols, G, float(eps),
+                             _ptr(y[lo * cols:hi * cols]), _ptr(partial[lo * gpr:hi * gpr]), _ptr(rstd[lo:hi]))
+
+    _run_blocks(run, _row_blocks(rows, threads), threads)
+    return y, partial, rstd

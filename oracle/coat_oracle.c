@@ -546,3 +546,40 @@ void orc_swiglu_absmax(const uint16_t *gate, const uint16_t *up, int64_t rows, i
             partial[r * gpr + j] = (float)mx;
         }
 }
+
+/* ======================================================================== */
+/* RMSNorm producer with Group Scaling stage 1 in its epilogue               */
+/* [COAT] "why activations are hard": the normalization layers are among the */
+/* nonlinear layers that hold most of the activation memory; "mixed          */
+/* granularity": stage 1 of the following linear layer's per-tensor scale is */
+/* taken where its input is produced.  RMSNorm as usually defined:           */
+/*   rstd = 1 / sqrt(mean_i x_i^2 + eps),  y_i = x_i * rstd * w_i.           */
+/* ======================================================================== */
+
+void orc_rmsnorm_absmax(const uint16_t *x, const uint16_t *weight, int64_t rows, int64_t cols, int64_t G,
+                        float eps, uint16_t *y_bf16, float *partial, float *rstd)
+{
+    int64_t gpr = cols / G;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * cols;
+        double ss = 0.0;
+        for (int64_t i = 0; i < cols; ++i) {
+            double v = bf16_to_double(xr[i]);
+            ss += v * v;
+        }
+        double rs = 1.0 / sqrt(ss / (double)cols + (double)eps);
+        if (rstd) rstd[r] = (float)rs;
+        for (int64_t j = 0; j < gpr; ++j) {
+            double mx = 0.0;
+            for (int64_t i = j * G; i < (j + 1) * G; ++i) {
+                double y = bf16_to_double(xr[i]) * rs;
+                if (weight) y *= bf16_to_double(weight[i]);
+                uint16_t b = orc_bf16_rne((float)y);
+                y_bf16[r * cols + i] = b;
+                double a = fabs(bf16_to_double(b));
+                if (a > mx) mx = a;
+            }
+            partial[r * gpr + j] = (float)mx;
+        }
+    }
+}

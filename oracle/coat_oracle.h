@@ -147,6 +147,14 @@ double orc_silu(double x);
 void orc_swiglu_absmax(const uint16_t *gate, const uint16_t *up, int64_t rows, int64_t cols, int64_t G,
                        uint16_t *h_bf16, float *partial);
 
+/* RMSNorm with Group Scaling stage 1 fused into its epilogue: per row
+ * rstd = 1 / sqrt(mean x^2 + eps) and y = x * rstd * w (w = 1 when weight is
+ * NULL), in binary64, y rounded to FP32 and then BF16 (nearest even);
+ * partial[r*(cols/G)+j] = max |y| over slice j of row r (y as stored);
+ * rstd (may be NULL) receives fp32(rstd) per row. */
+void orc_rmsnorm_absmax(const uint16_t *x, const uint16_t *weight, int64_t rows, int64_t cols, int64_t G,
+                        float eps, uint16_t *y_bf16, float *partial, float *rstd);
+
 #ifdef __cplusplus
 }
 #endif
