@@ -54,6 +54,8 @@ def lib():
     L.coat_dequant_group.argtypes = [P, i64, i64, i32, P, P, P]
     L.coat_swiglu_fused.argtypes = [P, P, i64, i64, i32, P, P, P, P, P, P, P]
     L.coat_swiglu_fused.restype = ctypes.c_int
+    L.coat_rmsnorm_fused.argtypes = [P, P, i64, i64, ctypes.c_float, i32, P, P, P, P, P, P]
+    L.coat_rmsnorm_fused.restype = ctypes.c_int
     for f in (L.coat_adamw_step, L.coat_group_absmax, L.coat_absmax_reduce,
               L.coat_quant_per_tensor, L.coat_quant_group, L.coat_adamw_step_bf16,
               L.coat_dequant_per_tensor, L.coat_dequant_group):
@@ -195,3 +197,18 @@ def coat_swiglu_fused(gate_bf16, up_bf16, h_bf16, h_partial, saved=None, *, grou
                                    rows, cols, group_size, _ptr(h_bf16, _U16, "h_bf16", n),
                                    _ptr(h_partial, _F32, "h_partial", ng), *sv, _stream(stream)),
            "coat_swiglu_fused")
+
+
+def coat_rmsnorm_fused(x_bf16, weight_bf16, y_bf16, y_partial, rstd=None, saved=None, *, eps: float = 1e-5,
+                       group_size: int = 128, stream=None) -> None:
+    """y = rmsnorm(x) * w (BF16) with the per-1xG maxima of y (Group Scaling
+    stage 1); rstd (FP32 [rows]) and saved = (x_codes, x_scales) optionally
+    keep what the backward pass needs, x in 1xG E4M3."""
+    rows, cols = x_bf16.shape
+    n, ng = rows * cols, rows * (cols // group_size)
+    xc, xs = (None, None) if saved is None else saved
+    _check(lib().coat_rmsnorm_fused(_ptr(x_bf16, _U16, "x_bf16", n), _ptr(weight_bf16, _U16, "weight_bf16", cols),
+                                    rows, cols, float(eps), group_size, _ptr(y_bf16, _U16, "y_bf16", n),
+                                    _ptr(y_partial, _F32, "y_partial", ng), _ptr(rstd, _F32, "rstd", rows),
+                                    _ptr(xc, _U8, "x_codes", n), _ptr(xs, _F32, "x_scales", ng), _stream(stream)),
+           "coat_rmsnorm_fused")

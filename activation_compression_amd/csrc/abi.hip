@@ -194,4 +194,20 @@ coat_status coat_swiglu_fused(const uint16_t *gate_bf16, const uint16_t *up_bf16
                                               gate_codes, gate_scales, up_codes, up_scales, (hipStream_t)stream));
 }
 
+coat_status coat_rmsnorm_fused(const uint16_t *x_bf16, const uint16_t *weight_bf16, int64_t rows, int64_t cols,
+                               float eps, int32_t group_size, uint16_t *y_bf16, float *y_partial_amax, float *rstd,
+                               uint8_t *x_codes, float *x_scales, void *stream) {
+    if (!x_bf16 || !y_bf16 || !y_partial_amax) return COAT_ERR_NULL;
+    if (!x_codes != !x_scales) return COAT_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16) || !aligned(y_partial_amax, 4) ||
+        (weight_bf16 && !aligned(weight_bf16, 16)) || (rstd && !aligned(rstd, 4)) ||
+        (x_codes && (!aligned(x_codes, 16) || !aligned(x_scales, 4))))
+        return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || cols > coat::kRmsNormMaxCols) return COAT_ERR_SHAPE;
+    if (!(eps > 0.0f) || !(eps < INFINITY)) return COAT_ERR_HPARAM;
+    return from_hip(coat::launch_rmsnorm_fused(x_bf16, weight_bf16, rows, (int)cols, group_size, eps, y_bf16,
+                                               y_partial_amax, rstd, x_codes, x_scales, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -54,6 +54,10 @@ hipError_t launch_quant_group(const uint16_t *x, int64_t n, int group_size, uint
                               float *scales, float *partial, hipStream_t stream, int num_cus);
 hipError_t launch_dequant_per_tensor(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
                                      hipStream_t stream);
+constexpr int kRmsNormMaxCols = 8192;  // one row per wave, held in registers
+hipError_t launch_rmsnorm_fused(const uint16_t *x, const uint16_t *weight, int64_t rows, int cols, int group_size,
+                                float eps, uint16_t *y, float *y_partial, float *rstd, uint8_t *x_codes,
+                                float *x_scales, hipStream_t stream);
 hipError_t launch_swiglu_fused(const uint16_t *gate, const uint16_t *up, int64_t n, int group_size, uint16_t *h,
                                float *h_partial, uint8_t *gate_codes, float *gate_scales, uint8_t *up_codes,
                                float *up_scales, hipStream_t stream);

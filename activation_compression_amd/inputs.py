@@ -197,6 +197,18 @@ def swiglu_up(rows: int = 16384, cols: int = 11008) -> ActivationSpec:
     return ActivationSpec(f"swiglu-up-{rows}x{cols}", rows, cols, seed=2003)
 
 
+def rmsnorm_input(rows: int = 16384, cols: int = 4096) -> ActivationSpec:
+    """Input of the normalization before a linear layer, [16384 tokens x 4096]."""
+    return ActivationSpec(f"rmsnorm-in-{rows}x{cols}", rows, cols, seed=2004)
+
+
+def gen_norm_weight(cols: int, seed: int = 2005, device="cpu") -> torch.Tensor:
+    """BF16 normalization gain [cols] as int16 bit patterns: 1 + 0.1 N(0, 1)."""
+    g = _gen(seed, torch.device(device))
+    w = 1.0 + 0.1 * torch.randn(cols, generator=g, device=torch.device(device))
+    return _bf16_bits(w)
+
+
 def outlier_channels(spec: ActivationSpec) -> torch.Tensor:
     g = _gen(spec.seed + 1, "cpu")
     return torch.randperm(spec.cols, generator=g)[: spec.n_outlier_channels]

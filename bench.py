@@ -17,8 +17,8 @@ bounded sample of the same step, on the host's cores.
 
 Beside the step (not in `value`), "extras" times the other entry points on
 the same resident workloads: the step with its BF16 working copy, the fused
-SwiGLU producer with Group Scaling stage 1 in its epilogue, and the FP8 ->
-BF16 activation dequantization.
+SwiGLU and RMSNorm producers with Group Scaling stage 1 in their epilogues,
+and the FP8 -> BF16 activation dequantization.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
 """
@@ -136,9 +136,9 @@ def entry(alg_bytes, ms, elems=None):
 def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     """The entry points beside the timed step, each timed alone on the same
     HBM-resident workloads: the step with its BF16 working-copy output; the
-    fused SwiGLU producer (stage 1 in its epilogue, with and without saving
-    its inputs in 1xG E4M3), against SwiGLU followed by a separate stage-1
-    pass over h; and the FP8 -> BF16 dequantization of saved activations."""
+    fused SwiGLU and RMSNorm producers (stage 1 in the epilogue, with and
+    without saving the inputs in 1xG E4M3), against the same op followed by
+    a separate stage-1 pass over its output; and the FP8 -> BF16 dequantization of saved activations."""
     import torch
 
     out = {}
@@ -172,6 +172,27 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
         "ms": round(ms_f + ms_a, 4), "algorithmic_bytes": int(8 * N + 8 * N / G),
         "stage1_share_fused": round(4 * N / G / (6 * N + 4 * N / G), 4),
         "stage1_share_separate": round(ms_a / (ms_f + ms_a), 4)}
+
+    rs = inputs.rmsnorm_input()
+    Nr = rs.numel
+    x = inputs.gen_activation(rs, device="cuda")
+    w = inputs.gen_norm_weight(rs.cols, device="cuda")
+    y = torch.empty(Nr, dtype=torch.int16, device="cuda")
+    yp = torch.empty(Nr // G, device="cuda")
+    rstd = torch.empty(rs.rows, device="cuda")
+    xsave = (torch.empty(Nr, dtype=torch.uint8, device="cuda"), torch.empty(Nr // G, device="cuda"))
+    ms_r = time_launches(lambda i: coat.coat_rmsnorm_fused(x, w, y, yp, rstd, None, group_size=G), reps)
+    ms_rs = time_launches(lambda i: coat.coat_rmsnorm_fused(x, w, y, yp, rstd, xsave, group_size=G), reps)
+    ms_ra = time_launches(lambda i: coat.coat_group_absmax(y.view(rs.rows, rs.cols), yp, amax, group_size=G), reps)
+    rshape = f"{rs.rows}x{rs.cols}"
+    base_r = 4 * Nr + 4 * Nr / G + 4 * rs.rows + 2 * rs.cols
+    out[f"rmsnorm_fused_{rshape}"] = entry(base_r, ms_r, Nr)
+    out[f"rmsnorm_fused_save_input_{rshape}"] = entry(base_r + Nr + 4 * Nr / G, ms_rs, Nr)
+    out[f"rmsnorm_then_separate_stage1_{rshape}"] = {
+        "ms": round(ms_r + ms_ra, 4), "algorithmic_bytes": int(base_r + 2 * Nr + 4 * Nr / G),
+        "stage1_share_fused": round(4 * Nr / G / base_r, 4),
+        "stage1_share_separate": round(ms_ra / (ms_r + ms_ra), 4)}
+    del x, w, y, yp, rstd, xsave
 
     codes, scales = saved[0], saved[1]
     out16 = h

@@ -229,6 +229,36 @@ coat_status coat_swiglu_fused(const uint16_t *gate_bf16, const uint16_t *up_bf16
                               uint8_t *gate_codes, float *gate_scales, uint8_t *up_codes, float *up_scales,
                               void *stream);
 
+/*
+ * coat_rmsnorm_fused -- RMSNorm with Group Scaling stage 1 fused into its
+ * epilogue ([COAT] "why activations are hard": normalization layers are among
+ * the nonlinear layers that dominate activation memory; [COAT] "mixed
+ * granularity": stage 1 is taken by the op that produces the tensor, and the
+ * normalization's input is saved in 1xG groups along the channel axis).
+ *   rstd = 1 / sqrt(mean_c x^2 + eps) per row, y = x * rstd * w, FP32, y
+ *   stored as BF16 (round to nearest even); y_partial_amax[r*(cols/G)+j] =
+ *   max |y| over slice j of row r (as stored).  coat_absmax_reduce then gives
+ *   the tensor absmax for coat_quant_per_tensor of y (the next linear layer's
+ *   input).  Optionally, in the same pass, x is saved for the backward pass as
+ *   1xG E4M3 exactly as coat_quant_group would write it, and rstd per row.
+ *
+ * x_bf16        BF16 [rows x cols] row-major, read only.  16-byte aligned.
+ * weight_bf16   BF16 [cols] gain, or NULL for none.  16-byte aligned.
+ * eps           > 0 and finite (else COAT_ERR_HPARAM).
+ * y_bf16        BF16 [rows x cols], written.  16-byte aligned.
+ * y_partial_amax  FP32 [rows * cols / G], written.
+ * rstd          FP32 [rows] or NULL.
+ * x_codes, x_scales  E4M3 [rows x cols] (16-byte aligned) and FP32
+ *               [rows * cols / G], both NULL or both set (else COAT_ERR_NULL).
+ * rows > 0; cols % G == 0 and cols <= 8192 (one row is held by one wave),
+ * else COAT_ERR_SHAPE.  The row's sum of squares is taken in FP32, so y
+ * agrees with a binary64 evaluation rounded to FP32 and then BF16 to within
+ * one BF16 step.
+ */
+coat_status coat_rmsnorm_fused(const uint16_t *x_bf16, const uint16_t *weight_bf16, int64_t rows, int64_t cols,
+                               float eps, int32_t group_size, uint16_t *y_bf16, float *y_partial_amax,
+                               float *rstd, uint8_t *x_codes, float *x_scales, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *coat_status_string(coat_status s);
 

@@ -30,7 +30,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for want in ("coat_adamw_step", "coat_adamw_step_bf16", "coat_group_absmax", "coat_absmax_reduce",
                  "coat_quant_per_tensor", "coat_quant_group", "coat_dequant_per_tensor",
-                 "coat_dequant_group", "coat_swiglu_fused", "coat_status_string"):
+                 "coat_dequant_group", "coat_swiglu_fused", "coat_rmsnorm_fused", "coat_status_string"):
         assert want in names
 
 
@@ -130,3 +130,19 @@ def test_swiglu_validates(L):
     assert L.coat_swiglu_fused(f, P(FAKE + 2), 4, 256, 128, f, f, None, None, None, None, None) == 2
     assert L.coat_swiglu_fused(f, f, 4, 200, 128, f, f, None, None, None, None, None) == 3
     assert L.coat_swiglu_fused(f, f, 4, 256, 96, f, f, None, None, None, None, None) == 4
+
+
+def test_rmsnorm_validates(L):
+    P, F = ctypes.c_void_p, ctypes.c_float
+    f = P(FAKE)
+    call = lambda x=f, w=None, rows=4, cols=256, eps=1e-5, G=128, xc=None, xs=None, y=f: L.coat_rmsnorm_fused(
+        x, w, rows, cols, F(eps), G, y, f, None, xc, xs, None)
+    assert call(x=P(0)) == 1
+    assert call(xc=f) == 1  # codes without scales
+    assert call(w=P(FAKE + 8)) == 2
+    assert call(cols=200) == 3
+    assert call(cols=16384, G=1024) == 3  # a row must fit one wave
+    assert call(rows=0) == 3
+    assert call(G=48) == 4
+    assert call(eps=0.0) == 6
+    assert call(eps=float("nan")) == 6

@@ -312,3 +312,84 @@ def test_swiglu_fused_full_size():
     h, hp, saved = gpu_swiglu(gate, up, 128, True)
     frac = check_swiglu(gate, up, 128, h, hp, saved, "16384x11008", threads=THREADS)
     flush(f"h identical fraction {frac:.7f}")
+
+
+# --------------------------------------------------------- fused RMSNorm (f1)
+def rstd_tol(cols):
+    """Relative bound on the kernel's FP32 rstd: a lane sums up to cols/64
+    squares in sequence and the wave adds 6 levels (positive terms: at most
+    (n - 1) u each), halved by the square root, plus the rounding of the
+    divide, add, square root and reciprocal."""
+    per_lane = -(-cols // 64)
+    return (0.5 * (per_lane + 6) + 4) * 2.0 ** -24
+
+
+def gpu_rmsnorm(x, w, G, eps, save):
+    rows, cols = x.shape
+    n, ng = rows * cols, rows * cols // G
+    y = torch.empty(n, dtype=torch.int16, device="cuda")
+    yp = torch.empty(ng, device="cuda")
+    rstd = torch.empty(rows, device="cuda")
+    saved = (torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(ng, device="cuda")) if save else None
+    xd = dev(x) if isinstance(x, np.ndarray) else x
+    wd = None if w is None else (dev(w) if isinstance(w, np.ndarray) else w)
+    coat.coat_rmsnorm_fused(xd, wd, y, yp, rstd, saved, eps=eps, group_size=G)
+    torch.cuda.synchronize()
+    return host(y), host(yp), host(rstd), None if saved is None else [host(t) for t in saved]
+
+
+def check_rmsnorm(x, w, G, eps, y, yp, rstd, saved, what, threads=1):
+    rows, cols = x.shape
+    y_ref, p_ref, r_ref = orc.rmsnorm_absmax(x, w, G, eps, threads=threads)
+    rel = np.abs(rstd.astype(np.float64) - r_ref) / r_ref
+    assert rel.max() <= rstd_tol(cols), f"{what}: rstd rel {rel.max():.3g}"
+    yg, yr = bf16_f32(y), bf16_f32(y_ref)
+    ok = np.abs(yg - yr) <= bf16_step(yr)
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond one BF16 step"
+    frac = np.count_nonzero(y == y_ref) / y.size
+    assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
+    assert (yp == np.abs(yg).reshape(-1, G).max(axis=1)).all(), what
+    assert (np.abs(yp - p_ref) <= bf16_step(p_ref)).all(), what
+    if saved is not None:
+        rc, rs, _ = orc.quant_group(x, G, threads=threads)
+        assert (norm0(saved[0]) == rc).all() and (saved[1] == rs).all(), what
+    return frac
+
+
+@pytest.mark.parametrize("rows, cols, G", [(40, 1024, 128), (13, 4096, 32), (7, 8192, 1024), (5, 2080, 32),
+                                           (9, 3072, 512)])
+@pytest.mark.parametrize("weighted, save", [(False, False), (True, True)])
+def test_rmsnorm_fused_small(rows, cols, G, weighted, save):
+    """(5, 2080) ends in a partial 64-piece sweep; (7, 8192) is the widest row."""
+    x = act(rows, cols, seed=rows * 7 + G)
+    x[1] = 0                  # zero row: y = 0, rstd = 1/sqrt(eps)
+    x[2, :G] = 0x8000         # a -0 slice
+    w = inputs.gen_norm_weight(cols, seed=cols).numpy().view(np.uint16) if weighted else None
+    flush(f"rmsnorm {rows}x{cols} G={G} weighted={weighted} save={save}")
+    y, yp, rstd, saved = gpu_rmsnorm(x, w, G, 1e-5, save)
+    check_rmsnorm(x, w, G, 1e-5, y, yp, rstd, saved, f"{rows}x{cols}")
+
+
+def test_rmsnorm_then_per_tensor_cast():
+    """Stage 1 from the norm's epilogue feeds stage 2 and the per-tensor cast
+    exactly as an unfused coat_group_absmax of the same y would."""
+    x = act(64, 4096, seed=41)
+    y, yp, _, _ = gpu_rmsnorm(x, None, 128, 1e-6, False)
+    amax = torch.empty(1, device="cuda")
+    coat.coat_absmax_reduce(dev(yp), amax)
+    partial2, amax2 = gpu_group_absmax(y.reshape(64, 4096), 128)
+    torch.cuda.synchronize()
+    assert (partial2 == yp).all() and host(amax)[0] == amax2
+
+
+@pytest.mark.slow
+def test_rmsnorm_fused_full_size():
+    """[16384 x 4096] with an x100 outlier channel, BF16 gain, input saved, in
+    the launch configuration timed."""
+    spec = inputs.rmsnorm_input()
+    x = inputs.gen_activation(spec).numpy().view(np.uint16)
+    w = inputs.gen_norm_weight(spec.cols).numpy().view(np.uint16)
+    flush(f"fused rmsnorm on {spec.name}")
+    y, yp, rstd, saved = gpu_rmsnorm(x, w, 128, 1e-5, True)
+    frac = check_rmsnorm(x, w, 128, 1e-5, y, yp, rstd, saved, spec.name, threads=THREADS)
+    flush(f"y identical fraction {frac:.7f}")
