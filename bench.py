@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_fp8_step-olmo7b-pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_fp8_step-olmo7b.md")
 
 
 def log(msg):
