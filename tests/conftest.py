@@ -40,7 +40,7 @@ def pytest_sessionfinish(session, exitstatus):
         import parity
     except Exception:
         return
-    if not parity.STATS:
+    if not parity.STATS and not parity.BF16_STATS:
         return
     import json
     out = os.path.join(ROOT, "gpurun_out")
@@ -50,6 +50,8 @@ def pytest_sessionfinish(session, exitstatus):
     with open(os.path.join(out, "parity_code_stats.json"), "w") as f:
         json.dump({"elements_compared": tot_n, "mismatching_codes": tot_bad,
                    "mismatch_fraction": tot_bad / max(tot_n, 1),
-                   "max_grid_steps": max(r[3] for r in parity.STATS),
+                   "max_grid_steps": max((r[3] for r in parity.STATS), default=0),
                    "per_comparison": [{"what": w, "n": n, "mismatches": b, "max_grid_steps": st}
-                                      for w, n, b, st in parity.STATS]}, f, indent=1)
+                                      for w, n, b, st in parity.STATS],
+                   "bf16_outputs": [{"what": w, "n": n, "not_identical": b, "not_identical_fraction": b / max(n, 1)}
+                                    for w, n, b in parity.BF16_STATS]}, f, indent=1)

@@ -51,6 +51,7 @@ LR, B1, B2, EPS, WD = (float(np.float32(v)) for v in
 THREADS = 8
 CODE_MATCH_MIN = 0.9999
 STATS = []  # (what, elements, mismatching codes) of every code comparison, for the report
+BF16_STATS = []  # (what, elements, elements not bit-identical) of every BF16 output compared in value space
 
 
 def flush(msg: str):

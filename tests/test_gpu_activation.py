@@ -6,6 +6,7 @@ import torch
 
 import oracle as orc
 from activation_compression_amd import coat, inputs
+import parity
 from parity import THREADS, dev, flush, host
 
 pytestmark = [pytest.mark.gpu,
@@ -232,6 +233,7 @@ def assert_h_close(h_gpu, h_ref, gate, up, what):
     ok = flushed | (np.abs(hg - hr) <= bf16_step(hr))
     assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond one BF16 step"
     same = (h_gpu == h_ref) | flushed
+    parity.BF16_STATS.append((what, same.size, int(same.size - np.count_nonzero(same))))
     frac = np.count_nonzero(same) / same.size
     assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
     return frac
@@ -310,7 +312,7 @@ def test_swiglu_fused_full_size():
     up = inputs.gen_activation(us).numpy().view(np.uint16)
     flush(f"fused swiglu on {gs.name}")
     h, hp, saved = gpu_swiglu(gate, up, 128, True)
-    frac = check_swiglu(gate, up, 128, h, hp, saved, "16384x11008", threads=THREADS)
+    frac = check_swiglu(gate, up, 128, h, hp, saved, "swiglu 16384x11008", threads=THREADS)
     flush(f"h identical fraction {frac:.7f}")
 
 
@@ -347,6 +349,7 @@ def check_rmsnorm(x, w, G, eps, y, yp, rstd, saved, what, threads=1):
     ok = np.abs(yg - yr) <= bf16_step(yr)
     assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond one BF16 step"
     frac = np.count_nonzero(y == y_ref) / y.size
+    parity.BF16_STATS.append((f"rmsnorm {what}", y.size, int(y.size - np.count_nonzero(y == y_ref))))
     assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
     assert (yp == np.abs(yg).reshape(-1, G).max(axis=1)).all(), what
     assert (np.abs(yp - p_ref) <= bf16_step(p_ref)).all(), what
