@@ -20,6 +20,7 @@ E4M3, E5M2 = 0, 1
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 
 _lib = None
+_P = ctypes.c_void_p
 
 
 class CoatError(RuntimeError):
@@ -31,6 +32,12 @@ class AdamWHParams(ctypes.Structure):
         ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
         ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
     ]
+
+
+class AdamWTensor(ctypes.Structure):
+    """coat_adamw_tensor: one tensor's optimizer-state buffers (device pointers)."""
+    _fields_ = [("param", _P), ("grad_bf16", _P), ("m_codes", _P), ("m_amax", _P), ("m_k", _P),
+                ("v_codes", _P), ("v_amax", _P), ("v_k", _P), ("param_bf16", _P), ("n", ctypes.c_int64)]
 
 
 def lib():
@@ -60,6 +67,12 @@ def lib():
               L.coat_quant_per_tensor, L.coat_quant_group, L.coat_adamw_step_bf16,
               L.coat_dequant_per_tensor, L.coat_dequant_group):
         f.restype = ctypes.c_int
+    L.coat_adamw_list_bytes.argtypes = [i32]
+    L.coat_adamw_list_bytes.restype = i64
+    L.coat_adamw_list_pack.argtypes = [ctypes.POINTER(AdamWTensor), i32, i32, P]
+    L.coat_adamw_list_pack.restype = ctypes.c_int
+    L.coat_adamw_step_list.argtypes = [P, P, ctypes.c_int, ctypes.POINTER(AdamWHParams), P]
+    L.coat_adamw_step_list.restype = ctypes.c_int
     L.coat_status_string.argtypes = [ctypes.c_int]
     L.coat_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -212,3 +225,41 @@ def coat_rmsnorm_fused(x_bf16, weight_bf16, y_bf16, y_partial, rstd=None, saved=
                                     _ptr(y_partial, _F32, "y_partial", ng), _ptr(rstd, _F32, "rstd", rows),
                                     _ptr(xc, _U8, "x_codes", n), _ptr(xs, _F32, "x_scales", ng), _stream(stream)),
            "coat_rmsnorm_fused")
+
+
+class AdamWTensorList:
+    """A packed tensor-list table (host and device copies) for
+    coat_adamw_step_list.  `states` is a sequence of dicts with the keys
+    param, grad, m_codes, m_amax, m_k, v_codes, v_amax, v_k and optionally
+    param_bf16 (device tensors, one allocation each is fine).  Build it once;
+    it stays valid while those tensors live, and keeps references to them."""
+
+    def __init__(self, states, *, group_size: int = 128):
+        n_t = len(states)
+        arr = (AdamWTensor * max(n_t, 1))()
+        for i, s in enumerate(states):
+            n = s["param"].numel()
+            ng = n // group_size
+            arr[i] = AdamWTensor(
+                _ptr(s["param"], _F32, "param", n), _ptr(s["grad"], _U16, "grad", n),
+                _ptr(s["m_codes"], _U8, "m_codes", n), _ptr(s["m_amax"], _F32, "m_amax", ng),
+                _ptr(s["m_k"], _F32, "m_k", ng), _ptr(s["v_codes"], _U8, "v_codes", n),
+                _ptr(s["v_amax"], _F32, "v_amax", ng), _ptr(s["v_k"], _F32, "v_k", ng),
+                _ptr(s.get("param_bf16"), _U16, "param_bf16", n), n)
+        nbytes = lib().coat_adamw_list_bytes(n_t)
+        if nbytes <= 0:
+            raise CoatError("coat_adamw_list_bytes: empty tensor list")
+        import numpy as np
+
+        self.host = np.zeros(nbytes, dtype=np.uint8)
+        _check(lib().coat_adamw_list_pack(arr, n_t, group_size, ctypes.c_void_p(self.host.ctypes.data)),
+               "coat_adamw_list_pack")
+        self.device = torch.from_numpy(self.host).to("cuda")
+        self.group_size = group_size
+        self._refs = list(states)
+
+
+def coat_adamw_step_list(tlist: AdamWTensorList, *, v_format="e4m3", hp: AdamWHParams, stream=None) -> None:
+    """One fused FP8-state AdamW step over every tensor of the list, one launch."""
+    _check(lib().coat_adamw_step_list(ctypes.c_void_p(tlist.host.ctypes.data), _ptr(tlist.device, _U8, "table"),
+                                      _FMT[v_format], ctypes.byref(hp), _stream(stream)), "coat_adamw_step_list")

@@ -58,46 +58,80 @@ const char *coat_status_string(coat_status s) {
 
 namespace {
 
+bool valid_hparams(const coat_adamw_hparams *hp) {
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
+    return isfinite(lr) && isfinite(wd) && isfinite(eps) && b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0 &&
+           eps > 0.0 && hp->step >= 1;
+}
+
+// Per-step scalars in binary64, rounded once.
+void make_params(const coat_adamw_hparams *hp, coat_fp8_format v_format, coat::StepParams &p) {
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, wd = hp->weight_decay;
+    const double t = (double)hp->step;
+    const double bc1 = 1.0 - pow(b1, t), bc2 = 1.0 - pow(b2, t);
+    p.beta1 = hp->beta1; p.omb1 = (float)(1.0 - b1);
+    p.beta2 = hp->beta2; p.omb2 = (float)(1.0 - b2);
+    p.step_size = (float)(lr / bc1);
+    p.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    p.eps = hp->eps;
+    p.decay = (float)(1.0 - lr * wd);
+    // log2 of each format's range MAX / smallest subnormal
+    p.m_log2_range = (float)(log2(448.0) + 9.0);
+    p.v_log2_range = v_format == COAT_FP8_E5M2 ? (float)(log2(57344.0) + 16.0) : p.m_log2_range;
+    memcpy(p.log_tab[0], coat::fp8_log_table(COAT_FP8_E4M3), sizeof p.log_tab[0]);
+    memcpy(p.log_tab[1], coat::fp8_log_table((int)v_format), sizeof p.log_tab[1]);
+}
+
+// One tensor's buffers: shared by the arena and tensor-list forms.
+coat_status check_bufs(const coat::StepBufs &b, int32_t group_size) {
+    if (!b.param || !b.grad || !b.m_codes || !b.m_amax || !b.m_k || !b.v_codes || !b.v_amax || !b.v_k)
+        return COAT_ERR_NULL;
+    if (!aligned(b.param, 16) || !aligned(b.grad, 16) || !aligned(b.m_codes, 16) || !aligned(b.v_codes, 16) ||
+        !aligned(b.m_amax, 4) || !aligned(b.m_k, 4) || !aligned(b.v_amax, 4) || !aligned(b.v_k, 4) ||
+        (b.param_bf16 && !aligned(b.param_bf16, 16)))
+        return COAT_ERR_ALIGN;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    if (b.n <= 0 || b.n % group_size != 0) return COAT_ERR_SHAPE;
+    return COAT_OK;
+}
+
 coat_status adamw_step_impl(float *param, const uint16_t *grad_bf16, uint8_t *m_codes, float *m_amax, float *m_k,
                             uint8_t *v_codes, float *v_amax, float *v_k, int64_t n, int32_t group_size,
                             coat_fp8_format v_format, const coat_adamw_hparams *hp, uint16_t *param_bf16,
                             void *stream) {
-    if (!param || !grad_bf16 || !m_codes || !m_amax || !m_k || !v_codes || !v_amax || !v_k || !hp)
-        return COAT_ERR_NULL;
-    if (!aligned(param, 16) || !aligned(grad_bf16, 16) || !aligned(m_codes, 16) || !aligned(v_codes, 16) ||
-        !aligned(m_amax, 4) || !aligned(m_k, 4) || !aligned(v_amax, 4) || !aligned(v_k, 4) ||
-        (param_bf16 && !aligned(param_bf16, 16)))
-        return COAT_ERR_ALIGN;
-    if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (n <= 0 || n % group_size != 0) return COAT_ERR_SHAPE;
-    if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
-    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
-    if (!isfinite(lr) || !isfinite(wd) || !isfinite(eps) || !(b1 >= 0.0 && b1 < 1.0) ||
-        !(b2 >= 0.0 && b2 < 1.0) || !(eps > 0.0) || hp->step < 1)
-        return COAT_ERR_HPARAM;
-
-    // per-step scalars in binary64, rounded once
-    const double t = (double)hp->step;
-    const double bc1 = 1.0 - pow(b1, t), bc2 = 1.0 - pow(b2, t);
     coat::StepArgs a;
-    a.param = param; a.grad = grad_bf16;
-    a.m_codes = m_codes; a.m_amax = m_amax; a.m_k = m_k;
-    a.v_codes = v_codes; a.v_amax = v_amax; a.v_k = v_k;
-    a.n = n;
+    a.buf = coat::StepBufs{param, grad_bf16, m_codes, m_amax, m_k, v_codes, v_amax, v_k, param_bf16, n};
+    if (!hp) return COAT_ERR_NULL;
+    const coat_status s = check_bufs(a.buf, group_size);
+    if (s != COAT_OK) return s;
+    if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
+    if (!valid_hparams(hp)) return COAT_ERR_HPARAM;
     a.n_chunks = coat::ceil_div(n, coat::kWaveElems);
-    a.beta1 = hp->beta1; a.omb1 = (float)(1.0 - b1);
-    a.beta2 = hp->beta2; a.omb2 = (float)(1.0 - b2);
-    a.step_size = (float)(lr / bc1);
-    a.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
-    a.eps = hp->eps;
-    a.decay = (float)(1.0 - lr * wd);
-    // log2 of each format's range MAX / smallest subnormal
-    a.m_log2_range = (float)(log2(448.0) + 9.0);
-    a.v_log2_range = v_format == COAT_FP8_E5M2 ? (float)(log2(57344.0) + 16.0) : a.m_log2_range;
-    memcpy(a.log_tab[0], coat::fp8_log_table(COAT_FP8_E4M3), sizeof a.log_tab[0]);
-    memcpy(a.log_tab[1], coat::fp8_log_table((int)v_format), sizeof a.log_tab[1]);
-    a.param_bf16 = param_bf16;
+    make_params(hp, v_format, a.p);
     return from_hip(coat::launch_adamw_fp8_step(a, group_size, (int)v_format, (hipStream_t)stream, num_cus()));
+}
+
+// Packed tensor-list table: header | int64 chunk_start[n + 1] (padded to 16
+// bytes) | StepBufs entries[n].  Written on the host by coat_adamw_list_pack;
+// the kernel reads the caller's device copy.
+struct ListHeader {
+    uint32_t magic;
+    uint32_t version;
+    int32_t n_tensors;
+    int32_t group_size;
+    int32_t has_bf16;
+    int32_t reserved;
+    int64_t total_chunks;
+};
+static_assert(sizeof(ListHeader) == 32, "list header layout");
+constexpr uint32_t kListMagic = 0x4C54414Fu;
+constexpr uint32_t kListVersion = 1;
+
+int64_t list_starts_bytes(int32_t n) { return (8 * ((int64_t)n + 1) + 15) / 16 * 16; }
+
+coat::StepBufs to_bufs(const coat_adamw_tensor &x) {
+    return coat::StepBufs{x.param, x.grad_bf16, x.m_codes, x.m_amax, x.m_k, x.v_codes, x.v_amax, x.v_k,
+                          x.param_bf16, x.n};
 }
 
 }  // namespace
@@ -208,6 +242,60 @@ coat_status coat_rmsnorm_fused(const uint16_t *x_bf16, const uint16_t *weight_bf
     if (!(eps > 0.0f) || !(eps < INFINITY)) return COAT_ERR_HPARAM;
     return from_hip(coat::launch_rmsnorm_fused(x_bf16, weight_bf16, rows, (int)cols, group_size, eps, y_bf16,
                                                y_partial_amax, rstd, x_codes, x_scales, (hipStream_t)stream));
+}
+
+int64_t coat_adamw_list_bytes(int32_t n_tensors) {
+    if (n_tensors <= 0) return 0;
+    return (int64_t)sizeof(ListHeader) + list_starts_bytes(n_tensors) + (int64_t)sizeof(coat::StepBufs) * n_tensors;
+}
+
+coat_status coat_adamw_list_pack(const coat_adamw_tensor *tensors, int32_t n_tensors, int32_t group_size,
+                                 void *table_host) {
+    if (!tensors || !table_host) return COAT_ERR_NULL;
+    if (n_tensors <= 0) return COAT_ERR_SHAPE;
+    if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    const bool bf16 = tensors[0].param_bf16 != nullptr;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const coat_status s = check_bufs(to_bufs(tensors[t]), group_size);
+        if (s != COAT_OK) return s;
+        if ((tensors[t].param_bf16 != nullptr) != bf16) return COAT_ERR_NULL;
+    }
+    unsigned char *out = static_cast<unsigned char *>(table_host);
+    unsigned char *starts = out + sizeof(ListHeader);
+    unsigned char *entries = starts + list_starts_bytes(n_tensors);
+    int64_t c = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const coat::StepBufs b = to_bufs(tensors[t]);
+        memcpy(starts + 8 * t, &c, sizeof c);
+        memcpy(entries + sizeof b * t, &b, sizeof b);
+        c += coat::ceil_div(b.n, coat::kWaveElems);
+    }
+    memcpy(starts + 8 * (int64_t)n_tensors, &c, sizeof c);
+    const ListHeader h{kListMagic, kListVersion, n_tensors, group_size, bf16 ? 1 : 0, 0, c};
+    memcpy(out, &h, sizeof h);
+    return COAT_OK;
+}
+
+coat_status coat_adamw_step_list(const void *table_host, const void *table_device, coat_fp8_format v_format,
+                                 const coat_adamw_hparams *hp, void *stream) {
+    if (!table_host || !table_device || !hp) return COAT_ERR_NULL;
+    if (!aligned(table_device, 16)) return COAT_ERR_ALIGN;
+    ListHeader h;
+    memcpy(&h, table_host, sizeof h);
+    if (h.magic != kListMagic || h.version != kListVersion || h.n_tensors <= 0 || h.total_chunks <= 0)
+        return COAT_ERR_SHAPE;
+    if (!valid_group(h.group_size)) return COAT_ERR_GROUP;
+    if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
+    if (!valid_hparams(hp)) return COAT_ERR_HPARAM;
+    const unsigned char *dev = static_cast<const unsigned char *>(table_device);
+    coat::StepListArgs a;
+    a.chunk_start = reinterpret_cast<const int64_t *>(dev + sizeof(ListHeader));
+    a.entries = reinterpret_cast<const coat::StepBufs *>(dev + sizeof(ListHeader) + list_starts_bytes(h.n_tensors));
+    a.total_chunks = h.total_chunks;
+    a.n_tensors = h.n_tensors;
+    a.has_bf16 = h.has_bf16;
+    make_params(hp, v_format, a.p);
+    return from_hip(coat::launch_adamw_fp8_step_list(a, h.group_size, (int)v_format, (hipStream_t)stream));
 }
 
 }  // extern "C"

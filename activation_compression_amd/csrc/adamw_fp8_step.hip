@@ -135,19 +135,20 @@ __device__ __forceinline__ float expand(float xs, float amq, float invq, float k
 // uniform).  kTail: the last, partial chunk -- lanes past n load nothing and
 // store nothing (their whole groups are past n as well, since n % G == 0).
 template <int G, int VF, bool kTail, bool kBf16>
-__device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab, int64_t base, int lane) {
+__device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &b, const float2 *tab, int64_t base,
+                                           int lane) {
     constexpr int LPG = G / 16;  // lanes per group (2 .. 64)
     const int j = lane & (LPG - 1);
     const bool v_lane = j == 1;  // lane 0 of a group computes m's parameters, lane 1 v's
-    const bool act = !kTail || base + lane * 16 < a.n;
+    const bool act = !kTail || base + lane * 16 < b.n;
     const int64_t gbase = base / G;  // first group of the chunk
     const int lgrp = lane / LPG;     // this lane's group within the chunk
 
     // wave-uniform bases, per-lane constant offsets
-    const float *pth = a.param + base;
-    const uint16_t *pg = a.grad + base;
-    const uint8_t *pmc = a.m_codes + base;
-    const uint8_t *pvc = a.v_codes + base;
+    const float *pth = b.param + base;
+    const uint16_t *pg = b.grad + base;
+    const uint8_t *pmc = b.m_codes + base;
+    const uint8_t *pvc = b.v_codes + base;
 
     float th[16];
     uint32_t gw[8], mw[4], vw[4];
@@ -167,8 +168,8 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
         const uint4 vc = reinterpret_cast<const uint4 *>(pvc)[lane];
         mw[0] = mc.x; mw[1] = mc.y; mw[2] = mc.z; mw[3] = mc.w;
         vw[0] = vc.x; vw[1] = vc.y; vw[2] = vc.z; vw[3] = vc.w;
-        am_m = a.m_amax[gbase + lgrp]; k_m = a.m_k[gbase + lgrp];
-        am_v = a.v_amax[gbase + lgrp]; k_v = a.v_k[gbase + lgrp];
+        am_m = b.m_amax[gbase + lgrp]; k_m = b.m_k[gbase + lgrp];
+        am_v = b.v_amax[gbase + lgrp]; k_v = b.v_k[gbase + lgrp];
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) th[i] = 0.0f;
@@ -195,11 +196,11 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
         const float v0 = dequant<false>(cv, tab + 256, am_v, am_v_ln2, ihv, ilv);
         const float g = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
 
-        const float m = __builtin_fmaf(a.beta1, m0, a.omb1 * g);
-        const float v = __builtin_fmaf(a.beta2, v0, a.omb2 * (g * g));
-        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(v), a.inv_sqrt_bc2, a.eps);
+        const float m = __builtin_fmaf(p.beta1, m0, p.omb1 * g);
+        const float v = __builtin_fmaf(p.beta2, v0, p.omb2 * (g * g));
+        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(v), p.inv_sqrt_bc2, p.eps);
         const float u = m * __builtin_amdgcn_rcpf(den);
-        th[i] = __builtin_fmaf(th[i], a.decay, -a.step_size * u);
+        th[i] = __builtin_fmaf(th[i], p.decay, -p.step_size * u);
         m1[i] = m;
         v1[i] = v;
 
@@ -209,12 +210,12 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
         mn_v = min(mn_v, (__float_as_uint(v) << 1) - 2u);
     }
     if (act) {
-        float4 *pp = reinterpret_cast<float4 *>(a.param + base) + lane * 4;
+        float4 *pp = reinterpret_cast<float4 *>(b.param + base) + lane * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             pp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
         if constexpr (kBf16) {  // the working copy the next forward pass reads
-            uint4 *bp = reinterpret_cast<uint4 *>(a.param_bf16 + base) + lane * 2;
+            uint4 *bp = reinterpret_cast<uint4 *>(b.param_bf16 + base) + lane * 2;
             bp[0] = make_uint4(bf16x2(th[0], th[1]), bf16x2(th[2], th[3]), bf16x2(th[4], th[5]),
                                bf16x2(th[6], th[7]));
             bp[1] = make_uint4(bf16x2(th[8], th[9]), bf16x2(th[10], th[11]), bf16x2(th[12], th[13]),
@@ -230,10 +231,10 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
 
     // one evaluation per lane: lane 0 of a group for m, lane 1 for v, then broadcast
     const GroupQ q = group_q(v_lane ? gx_v : gx_m, v_lane ? gn_v : gn_m,
-                             v_lane ? a.v_log2_range : a.m_log2_range);
+                             v_lane ? p.v_log2_range : p.m_log2_range);
     if (act && j < 2) {
-        (v_lane ? a.v_amax : a.m_amax)[gbase + lgrp] = q.amax;
-        (v_lane ? a.v_k : a.m_k)[gbase + lgrp] = q.k;
+        (v_lane ? b.v_amax : b.m_amax)[gbase + lgrp] = q.amax;
+        (v_lane ? b.v_k : b.m_k)[gbase + lgrp] = q.k;
     }
     const float amq_m = run_bcast<LPG, 0>(q.amq), inv_m = run_bcast<LPG, 0>(q.invq);
     const float kq_m = run_bcast<LPG, 0>(q.k);
@@ -272,30 +273,61 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const float2 *tab,
         }
     }
     if (act) {
-        reinterpret_cast<uint4 *>(a.m_codes + base)[lane] = make_uint4(om[0], om[1], om[2], om[3]);
-        reinterpret_cast<uint4 *>(a.v_codes + base)[lane] = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+        reinterpret_cast<uint4 *>(b.m_codes + base)[lane] = make_uint4(om[0], om[1], om[2], om[3]);
+        reinterpret_cast<uint4 *>(b.v_codes + base)[lane] = make_uint4(ov[0], ov[1], ov[2], ov[3]);
     }
+}
+
+// The per-code dequantization table in LDS: [0, 256) m codes (E4M3), [256, 512)
+// v codes, both signs of a code byte mapping to its magnitude's entry.
+__device__ __forceinline__ void fill_tab(float2 *tab, const StepParams &p) {
+    const uint32_t t = threadIdx.x;
+    tab[t] = p.log_tab[0][t & 127u];
+    tab[256 + t] = p.log_tab[1][t & 127u];
+    __syncthreads();
 }
 
 template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a) {
-    // Per code byte (both signs): [0, 256) m codes (E4M3), [256, 512) v codes.
     __shared__ float2 tab[512];
-    {
-        const uint32_t t = threadIdx.x;
-        tab[t] = a.log_tab[0][t & 127u];
-        tab[256 + t] = a.log_tab[1][t & 127u];
-    }
-    __syncthreads();
-
+    fill_tab(tab, a.p);
     const int lane = threadIdx.x & 63;
     const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (chunk >= a.n_chunks) return;
-    if (chunk < a.n / kWaveElems)  // every lane in range
-        step_chunk<G, VF, false, kBf16>(a, tab, chunk * kWaveElems, lane);
+    if (chunk < a.buf.n / kWaveElems)  // every lane in range
+        step_chunk<G, VF, false, kBf16>(a.p, a.buf, tab, chunk * kWaveElems, lane);
     else
-        step_chunk<G, VF, true, kBf16>(a, tab, chunk * kWaveElems, lane);
+        step_chunk<G, VF, true, kBf16>(a.p, a.buf, tab, chunk * kWaveElems, lane);
+}
+
+// Tensor-list form: the launch numbers the chunks of all tensors in order; a
+// wave finds its tensor by binary search over chunk_start (wave-uniform, so
+// the loads are scalar and hit the scalar cache after the first waves), then
+// runs the same per-chunk step on that tensor's buffers.  A tensor's last
+// chunk is partial unless its size is a multiple of 1024.
+template <int G, int VF, bool kBf16>
+__global__ __launch_bounds__(kBlock) void adamw_fp8_step_list_kernel(const StepListArgs a) {
+    __shared__ float2 tab[512];
+    fill_tab(tab, a.p);
+    const int lane = threadIdx.x & 63;
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) +
+                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (chunk >= a.total_chunks) return;
+    int lo = 0, hi = a.n_tensors;  // chunk_start[lo] <= chunk < chunk_start[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.chunk_start[mid] <= chunk)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const StepBufs b = a.entries[lo];
+    const int64_t local = chunk - a.chunk_start[lo];
+    if (local < b.n / kWaveElems)
+        step_chunk<G, VF, false, kBf16>(a.p, b, tab, local * kWaveElems, lane);
+    else
+        step_chunk<G, VF, true, kBf16>(a.p, b, tab, local * kWaveElems, lane);
 }
 
 template <int G, int VF, bool kBf16>
@@ -306,8 +338,16 @@ hipError_t launch(const StepArgs &a, hipStream_t stream, int num_cus) {
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
 }
 
-template <int VF, bool kBf16>
-hipError_t launch_g(const StepArgs &a, int G, hipStream_t s, int cap) {
+template <int G, int VF, bool kBf16>
+hipError_t launch(const StepListArgs &a, hipStream_t stream, int) {
+    constexpr auto kernel = &adamw_fp8_step_list_kernel<G, VF, kBf16>;
+    const dim3 grid((unsigned)ceil_div(a.total_chunks, kBlock / 64));
+    void *args[] = {const_cast<StepListArgs *>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
+}
+
+template <int VF, bool kBf16, class Args>
+hipError_t launch_g(const Args &a, int G, hipStream_t s, int cap) {
     switch (G) {
     case 32: return launch<32, VF, kBf16>(a, s, cap);
     case 64: return launch<64, VF, kBf16>(a, s, cap);
@@ -351,11 +391,19 @@ const float2 *fp8_log_table(int fmt) {
 
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
                                  hipStream_t stream, int num_cus) {
-    if (a.param_bf16)
+    if (a.buf.param_bf16)
         return v_format == kE5M2 ? launch_g<kE5M2, true>(a, group_size, stream, num_cus)
                                  : launch_g<kE4M3, true>(a, group_size, stream, num_cus);
     return v_format == kE5M2 ? launch_g<kE5M2, false>(a, group_size, stream, num_cus)
                              : launch_g<kE4M3, false>(a, group_size, stream, num_cus);
+}
+
+hipError_t launch_adamw_fp8_step_list(const StepListArgs &a, int group_size, int v_format, hipStream_t stream) {
+    if (a.has_bf16)
+        return v_format == kE5M2 ? launch_g<kE5M2, true>(a, group_size, stream, 0)
+                                 : launch_g<kE4M3, true>(a, group_size, stream, 0);
+    return v_format == kE5M2 ? launch_g<kE5M2, false>(a, group_size, stream, 0)
+                             : launch_g<kE4M3, false>(a, group_size, stream, 0);
 }
 
 }  // namespace coat

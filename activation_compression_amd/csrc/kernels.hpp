@@ -7,17 +7,22 @@
 
 namespace coat {
 
-// Arguments of the fused FP8-state AdamW step, with the per-step scalars
-// already folded on the host (binary64, rounded once to FP32).
-struct StepArgs {
+// One tensor's (or one arena's) buffers for the fused FP8-state AdamW step.
+// Also the device layout of one entry of a tensor-list table (80 bytes).
+struct StepBufs {
     float *param;
     const uint16_t *grad;
     uint8_t *m_codes;
     float *m_amax, *m_k;
     uint8_t *v_codes;
     float *v_amax, *v_k;
-    int64_t n;            // parameters
-    int64_t n_chunks;     // ceil(n / 1024): one wave handles 1024 per pass
+    uint16_t *param_bf16;  // BF16 working copy of the updated weights, or null
+    int64_t n;             // parameters, a multiple of the group size
+};
+static_assert(sizeof(StepBufs) == 80, "tensor-list entry layout");
+
+// Per-step scalars, folded on the host (binary64, rounded once to FP32).
+struct StepParams {
     float beta1, omb1;    // beta1 and 1 - beta1 (exact in FP32 for beta1 in [0.5, 1))
     float beta2, omb2;
     float step_size;      // lr / (1 - beta1^t)
@@ -29,7 +34,26 @@ struct StepArgs {
     // log2(|decode(c)| / MAX) for every code magnitude c, as an FP32 hi + lo
     // pair (code 0 and non-finite codes hold -2^100): m's format, then v's.
     float2 log_tab[2][128];
-    uint16_t *param_bf16;  // BF16 working copy of the updated weights, or null
+};
+
+// One flat arena, one launch.
+struct StepArgs {
+    StepBufs buf;
+    int64_t n_chunks;  // ceil(n / 1024): one wave handles 1024 per pass
+    StepParams p;
+};
+
+// A list of separately allocated tensors, one launch.  The table lives in
+// device memory: chunk_start[t] is the first 1024-parameter chunk of tensor t
+// in the launch's chunk numbering (chunk_start[0] = 0, chunk_start[n_tensors]
+// = total_chunks); entries[t] holds its buffers.
+struct StepListArgs {
+    const int64_t *chunk_start;
+    const StepBufs *entries;
+    int64_t total_chunks;
+    int32_t n_tensors;
+    int32_t has_bf16;  // every entry has a BF16 copy (else none has)
+    StepParams p;
 };
 
 // Fill tab[c] = log2(|decode(c)| / MAX) for the 128 code magnitudes of an OCP
@@ -43,6 +67,7 @@ const float2 *fp8_log_table(int fmt);
 // be resident at once.
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
                                  hipStream_t stream, int num_cus);
+hipError_t launch_adamw_fp8_step_list(const StepListArgs &a, int group_size, int v_format, hipStream_t stream);
 
 hipError_t launch_group_absmax(const uint16_t *x, int64_t n, int group_size, float *partial,
                                float *amax, hipStream_t stream, int num_cus);

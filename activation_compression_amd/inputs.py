@@ -81,6 +81,15 @@ def olmo_7b() -> ArenaSpec:
     return ArenaSpec("olmo-7b-shaped", 4, tuple(ts), "e4m3", 128, "tensor")
 
 
+def ragged_list(group_size: int = 128, v_fmt: str = "e4m3") -> ArenaSpec:
+    """Nine tensors of G x {1, 2, 7, 8, 9, 64, 100, 513, 1000} parameters: sizes
+    below, at and between multiples of the 1024-parameter chunk, for the
+    tensor-list step (each tensor in its own allocation there)."""
+    ks = (1, 2, 7, 8, 9, 64, 100, 513, 1000)
+    return ArenaSpec(f"ragged-list-G{group_size}-{v_fmt}", 6,
+                     tuple((f"t{i}", (k, group_size)) for i, k in enumerate(ks)), v_fmt, group_size, "tensor")
+
+
 def stress(group_size: int = 128, v_fmt: str = "e4m3", numel: int = 64 << 20) -> ArenaSpec:
     """64 Mi parameters with gradients spanning ten decades (and 5% zeros)."""
     cols = 1 << 13

@@ -16,8 +16,9 @@ HIP events on the stream it runs on.  The CPU baseline is the oracle on a
 bounded sample of the same step, on the host's cores.
 
 Beside the step (not in `value`), "extras" times the other entry points on
-the same resident workloads: the step with its BF16 working copy, the fused
-SwiGLU and RMSNorm producers with Group Scaling stage 1 in their epilogues,
+the same resident workloads: the step with its BF16 working copy, the step as a
+tensor-list launch (one entry per model tensor), the fused SwiGLU and RMSNorm
+producers with Group Scaling stage 1 in their epilogues,
 and the FP8 -> BF16 activation dequantization.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
@@ -136,6 +137,7 @@ def entry(alg_bytes, ms, elems=None):
 def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     """The entry points beside the timed step, each timed alone on the same
     HBM-resident workloads: the step with its BF16 working-copy output; the
+    step as a tensor-list launch over the model's tensors; the
     fused SwiGLU and RMSNorm producers (stage 1 in the epilogue, with and
     without saving the inputs in 1xG E4M3), against the same op followed by
     a separate stage-1 pass over its output; and the FP8 -> BF16 dequantization of saved activations."""
@@ -152,6 +154,19 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
         group_size=G, v_format=spec.v_fmt, hp=hp(step0 + i)), 3)
     out["adamw_fp8_step_bf16_copy"] = entry(n * (16.0 + 32.0 / G), ms, n)
     del wcopy
+
+    # the same step through the tensor-list launch: one entry per tensor of
+    # the model (views of the arena, so the bytes are the same), one launch
+    views = []
+    for _, off, m, _ in spec.offsets():
+        d = {"param": theta[off:off + m], "grad": grad[off:off + m]}
+        for k in ("m_codes", "m_amax", "m_k", "v_codes", "v_amax", "v_k"):
+            d[k] = st[k][off:off + m] if k.endswith("codes") else st[k][off // G:(off + m) // G]
+        views.append(d)
+    tl = coat.AdamWTensorList(views, group_size=G)
+    ms = time_launches(lambda i: coat.coat_adamw_step_list(tl, v_format=spec.v_fmt, hp=hp(step0 + 4 + i)), 3)
+    out[f"adamw_fp8_step_list_{len(views)}_tensors"] = entry(n * (14.0 + 32.0 / G), ms, n)
+    del tl, views
 
     gs, us = inputs.swiglu_gate(), inputs.swiglu_up()
     N = gs.numel

@@ -125,6 +125,53 @@ coat_status coat_adamw_step_bf16(float *param, const uint16_t *grad_bf16,
                                  const coat_adamw_hparams *hp, void *stream);
 
 /*
+ * Tensor-list form of the step: the parameters live in separate allocations
+ * (one per tensor, as a training framework keeps them) instead of one arena,
+ * and all of them are updated by ONE launch.  Each tensor follows exactly the
+ * per-group arithmetic of coat_adamw_step (the same update rule and expansion,
+ * [COAT] and [ATLAS] as cited there); since groups never straddle tensors,
+ * the result is bit for bit that of one coat_adamw_step call per tensor.
+ *
+ * Use: describe the tensors with coat_adamw_tensor entries; pack them once into
+ * a host table of coat_adamw_list_bytes(n) bytes (coat_adamw_list_pack
+ * validates every entry as coat_adamw_step would); copy that table, unchanged,
+ * into device memory the caller owns (16-byte aligned); then call
+ * coat_adamw_step_list with both copies every step.  The tables stay valid
+ * while the tensors stay where they are; the library keeps no pointer to them
+ * after a call returns, and the device copy must stay alive until the launch
+ * has run (stream order).
+ */
+typedef struct {
+    float *param;              /* FP32 [n], 16-byte aligned                    */
+    const uint16_t *grad_bf16; /* BF16 [n], 16-byte aligned                    */
+    uint8_t *m_codes;          /* E4M3 [n], 16-byte aligned                    */
+    float *m_amax, *m_k;       /* FP32 [n/G] each, 4-byte aligned              */
+    uint8_t *v_codes;          /* [n] in the list's v format, 16-byte aligned  */
+    float *v_amax, *v_k;       /* FP32 [n/G] each                              */
+    uint16_t *param_bf16;      /* BF16 working copy [n], or NULL: all entries of
+                                  a list NULL or all set (else COAT_ERR_NULL)   */
+    int64_t n;                 /* parameters, > 0, a multiple of G             */
+} coat_adamw_tensor;
+
+/* Size in bytes of the packed table for n_tensors tensors (0 if n_tensors <= 0). */
+int64_t coat_adamw_list_bytes(int32_t n_tensors);
+
+/* Validate tensors[0..n_tensors) for group size G and write the packed table to
+ * table_host (coat_adamw_list_bytes(n_tensors) bytes, any alignment).  Errors:
+ * COAT_ERR_NULL, _ALIGN, _GROUP, _SHAPE as coat_adamw_step per entry;
+ * n_tensors <= 0 -> COAT_ERR_SHAPE.  Nothing is written on error. */
+coat_status coat_adamw_list_pack(const coat_adamw_tensor *tensors, int32_t n_tensors, int32_t group_size,
+                                 void *table_host);
+
+/* One fused step over every tensor of a packed list.  table_host: the table
+ * coat_adamw_list_pack wrote (read during the call: launch size, G, whether a
+ * BF16 copy is written); table_device: its byte-identical device copy, read by
+ * the kernel.  v_format and hp as coat_adamw_step.  A table that does not carry
+ * the packer's header -> COAT_ERR_SHAPE. */
+coat_status coat_adamw_step_list(const void *table_host, const void *table_device, coat_fp8_format v_format,
+                                 const coat_adamw_hparams *hp, void *stream);
+
+/*
  * coat_group_absmax -- both stages of Group Scaling ([COAT] section "mixed
  * granularity"): stage 1 writes the max |x| of every 1xG slice of each row,
  * stage 2 reduces that G-times-smaller tensor to the tensor absmax.

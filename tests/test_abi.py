@@ -5,6 +5,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from conftest import ROOT
@@ -30,7 +32,8 @@ def test_header_declares_the_path():
     names = declared_functions()
     for want in ("coat_adamw_step", "coat_adamw_step_bf16", "coat_group_absmax", "coat_absmax_reduce",
                  "coat_quant_per_tensor", "coat_quant_group", "coat_dequant_per_tensor",
-                 "coat_dequant_group", "coat_swiglu_fused", "coat_rmsnorm_fused", "coat_status_string"):
+                 "coat_dequant_group", "coat_swiglu_fused", "coat_rmsnorm_fused", "coat_adamw_list_bytes",
+                 "coat_adamw_list_pack", "coat_adamw_step_list", "coat_status_string"):
         assert want in names
 
 
@@ -146,3 +149,85 @@ def test_rmsnorm_validates(L):
     assert call(G=48) == 4
     assert call(eps=0.0) == 6
     assert call(eps=float("nan")) == 6
+
+
+def _tensor(base, n, bf16=False):
+    from activation_compression_amd.coat import AdamWTensor
+    a = base
+    return AdamWTensor(a, a + 0x100000, a + 0x200000, a + 0x300000, a + 0x400000, a + 0x500000, a + 0x600000,
+                       a + 0x700000, a + 0x800000 if bf16 else None, n)
+
+
+def _list_lib():
+    from activation_compression_amd import coat
+    return coat.lib(), coat
+
+
+def test_list_bytes():
+    L, _ = _list_lib()
+    assert L.coat_adamw_list_bytes(0) == 0 and L.coat_adamw_list_bytes(-3) == 0
+    assert L.coat_adamw_list_bytes(1) == 32 + 16 + 80
+    assert L.coat_adamw_list_bytes(3) == 32 + 32 + 240
+    assert L.coat_adamw_list_bytes(130) == 32 + 1056 + 130 * 80
+
+
+def test_list_pack_layout():
+    """Header, chunk prefix (ceil(n/1024) per tensor, in order) and entries,
+    read back with numpy from the packed bytes."""
+    L, coat = _list_lib()
+    sizes = [128, 1024, 1152, 384, 2048 * 5 + 128]
+    arr = (coat.AdamWTensor * len(sizes))(*[_tensor(0x1000000 * (i + 1), n) for i, n in enumerate(sizes)])
+    buf = np.zeros(L.coat_adamw_list_bytes(len(sizes)), np.uint8)
+    assert L.coat_adamw_list_pack(arr, len(sizes), 128, ctypes.c_void_p(buf.ctypes.data)) == 0
+    hdr = buf[:32].view(np.int32)
+    assert hdr[2] == len(sizes) and hdr[3] == 128 and hdr[4] == 0
+    chunks = [-(-n // 1024) for n in sizes]
+    assert buf[24:32].view(np.int64)[0] == sum(chunks)
+    starts = buf[32:32 + 8 * (len(sizes) + 1)].view(np.int64)
+    assert list(starts) == list(np.concatenate([[0], np.cumsum(chunks)]))
+    ent = buf[32 + 48:].view(np.int64).reshape(len(sizes), 10)
+    for i, n in enumerate(sizes):
+        base = 0x1000000 * (i + 1)
+        assert list(ent[i, :8]) == [base + 0x100000 * j for j in range(8)]
+        assert ent[i, 8] == 0 and ent[i, 9] == n
+
+
+def test_list_pack_validates():
+    L, coat = _list_lib()
+    buf = np.zeros(4096, np.uint8)
+    out = ctypes.c_void_p(buf.ctypes.data)
+
+    def pack(ts, G=128):
+        arr = (coat.AdamWTensor * len(ts))(*ts)
+        return L.coat_adamw_list_pack(arr, len(ts), G, out)
+
+    good = _tensor(0x1000000, 1024)
+    assert pack([good, _tensor(0x2000000, 256)]) == 0
+    bad_null = _tensor(0x2000000, 256); bad_null.m_k = None
+    assert pack([good, bad_null]) == 1
+    assert pack([good, _tensor(0x2000008, 256)]) == 2     # param not 16-byte aligned
+    assert pack([good, _tensor(0x2000000, 200)]) == 3     # n % G
+    assert pack([good, _tensor(0x2000000, 0)]) == 3
+    assert pack([good], G=96) == 4
+    assert pack([good, _tensor(0x2000000, 256, bf16=True)]) == 1  # BF16 copy on some entries only
+    assert L.coat_adamw_list_pack((coat.AdamWTensor * 1)(good), 0, 128, out) == 3
+    assert L.coat_adamw_list_pack(None, 1, 128, out) == 1
+
+
+def test_step_list_validates_before_launch():
+    """Every error below is found on the host; nothing is launched."""
+    L, coat = _list_lib()
+    arr = (coat.AdamWTensor * 2)(_tensor(0x1000000, 1024), _tensor(0x2000000, 256))
+    buf = np.zeros(L.coat_adamw_list_bytes(2), np.uint8)
+    assert L.coat_adamw_list_pack(arr, 2, 128, ctypes.c_void_p(buf.ctypes.data)) == 0
+    host = ctypes.c_void_p(buf.ctypes.data)
+    hp = coat.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.1, 1)
+    devp = ctypes.c_void_p(FAKE)
+    assert L.coat_adamw_step_list(None, devp, 0, ctypes.byref(hp), None) == 1
+    assert L.coat_adamw_step_list(host, None, 0, ctypes.byref(hp), None) == 1
+    assert L.coat_adamw_step_list(host, ctypes.c_void_p(FAKE + 4), 0, ctypes.byref(hp), None) == 2
+    assert L.coat_adamw_step_list(host, devp, 7, ctypes.byref(hp), None) == 5
+    bad = coat.adamw_hparams(1e-3, 1.0, 0.999, 1e-8, 0.1, 1)
+    assert L.coat_adamw_step_list(host, devp, 0, ctypes.byref(bad), None) == 6
+    junk = np.zeros_like(buf)
+    assert L.coat_adamw_step_list(ctypes.c_void_p(junk.ctypes.data), devp, 0, ctypes.byref(hp), None) == 3

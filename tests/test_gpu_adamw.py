@@ -301,3 +301,119 @@ def test_step_with_bf16_working_copy(v_fmt):
         tol = 1e-6 * np.abs(th_r.astype(np.float64)) + 1e-6 * LR + np.spacing(np.abs(want).astype(np.float32)) * 2 ** 16
         assert (np.abs(got - want) <= tol).all()
         assert (got == want).mean() > 0.9999
+
+
+# ---------------------------------------------------- tensor-list launch (f4)
+STATE_KEYS = ("m_codes", "m_amax", "m_k", "v_codes", "v_amax", "v_k")
+
+
+def list_buffers(theta, g_bits, st, spec, bf16=False):
+    """Each tensor of `spec` in allocations of its own (copies of its slices)."""
+    G = spec.group_size
+    out = []
+    for _, off, n, _ in spec.offsets():
+        d = {"param": dev(theta[off:off + n]), "grad": dev(g_bits[off:off + n])}
+        for k in STATE_KEYS:
+            a = st[k]
+            d[k] = dev(a[off:off + n] if k.endswith("codes") else a[off // G:(off + n) // G])
+        if bf16:
+            d["param_bf16"] = torch.empty(n, dtype=torch.int16, device="cuda")
+        out.append(d)
+    return out
+
+
+def gather(bufs, key):
+    return np.concatenate([host(b[key]) for b in bufs])
+
+
+def gpu_list_step(theta, g_bits, st, spec, t, bf16=False):
+    bufs = list_buffers(theta, g_bits, st, spec, bf16)
+    tl = coat.AdamWTensorList(bufs, group_size=spec.group_size)
+    coat.coat_adamw_step_list(tl, v_format=spec.v_fmt, hp=gpu_hp(t))
+    torch.cuda.synchronize()
+    res = (gather(bufs, "param"), {k: gather(bufs, k) for k in STATE_KEYS})
+    return res, (gather(bufs, "param_bf16") if bf16 else None)
+
+
+def same_bits(a, b):
+    return a.dtype == b.dtype and a.shape == b.shape and (a.view(np.uint8) == b.view(np.uint8)).all()
+
+
+@pytest.mark.parametrize("G, v_fmt", [(128, "e4m3"), (32, "e5m2"), (1024, "e4m3"), (64, "e5m2")])
+def test_tensor_list_matches_arena_and_oracle(G, v_fmt):
+    """Nine tensors in separate allocations, sizes below, at and between
+    multiples of the 1024-parameter chunk, one launch: bit for bit the
+    arena step over their concatenation, and the oracle's step to the parity
+    bar; two steps in lockstep from the oracle's state."""
+    spec = inputs.ragged_list(G, v_fmt)
+    theta = inputs.gen_params(spec).numpy()
+    st = np_state(spec.numel, G)
+    for t in (1, 2):
+        g = inputs.gen_grads(spec, t).numpy().view(np.uint16)
+        flush(f"tensor list G={G} {v_fmt} step {t}")
+        lst, _ = gpu_list_step(theta, g, st, spec, t)
+        arena = gpu_step(theta, g, st, G, v_fmt, t)
+        assert same_bits(lst[0], arena[0])
+        for k in STATE_KEYS:
+            assert same_bits(lst[1][k], arena[1][k]), k
+        ref = oracle_step(theta, g, st, G, v_fmt, t)
+        assert_step_parity(lst, ref, v_fmt, f"list G={G} step {t}", prev=None if t == 1 else st)
+        theta, st = ref
+
+
+def test_tensor_list_with_bf16_copy():
+    spec = inputs.ragged_list(128, "e4m3")
+    theta = inputs.gen_params(spec).numpy()
+    st = np_state(spec.numel, 128)
+    g = inputs.gen_grads(spec, 1).numpy().view(np.uint16)
+    (th, s), copy = gpu_list_step(theta, g, st, spec, 1, bf16=True)
+    arena = gpu_step(theta, g, st, 128, "e4m3", 1)
+    assert same_bits(th, arena[0]) and all(same_bits(s[k], arena[1][k]) for k in STATE_KEYS)
+    want = torch.from_numpy(th).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (copy == want).all()
+
+
+def test_tensor_list_single_small_tensor():
+    """One tensor of one group: a launch of a single partial chunk."""
+    spec = inputs.ArenaSpec("one-group", 6, (("w", (1, 32)),), "e4m3", 32, "tensor")
+    theta = inputs.gen_params(spec).numpy()
+    g = inputs.gen_grads(spec, 1).numpy().view(np.uint16)
+    st = np_state(32, 32)
+    lst, _ = gpu_list_step(theta, g, st, spec, 1)
+    arena = gpu_step(theta, g, st, 32, "e4m3", 1)
+    assert same_bits(lst[0], arena[0]) and all(same_bits(lst[1][k], arena[1][k]) for k in STATE_KEYS)
+
+
+@pytest.mark.slow
+def test_olmo1b_shaped_tensor_list_bitwise_vs_arena():
+    """The 65 OLMo-1B-shaped tensors as separate allocations, one list launch
+    per step, against the arena step on the same values: identical bytes over
+    two steps, every element (compared on the device)."""
+    spec = inputs.olmo_1b()
+    G, n = spec.group_size, spec.numel
+    flush(f"generating {spec.name}")
+    th_a = inputs.gen_params(spec, device="cuda")
+    st_a = inputs.fresh_state(n, G, device="cuda")
+    bufs = []
+    for _, off, m, _ in spec.offsets():
+        d = {"param": th_a[off:off + m].clone(), "grad": torch.empty(m, dtype=torch.int16, device="cuda")}
+        for k in STATE_KEYS:
+            a = st_a[k]
+            d[k] = (a[off:off + m] if k.endswith("codes") else a[off // G:(off + m) // G]).clone()
+        bufs.append(d)
+    tl = coat.AdamWTensorList(bufs, group_size=G)
+    for t in (1, 2):
+        g_a = inputs.gen_grads(spec, t, device="cuda")
+        for (_, off, m, _), d in zip(spec.offsets(), bufs):
+            d["grad"].copy_(g_a[off:off + m])
+        flush(f"olmo-1b list vs arena step {t}")
+        _arena_step(th_a, g_a, st_a, spec, t)
+        coat.coat_adamw_step_list(tl, v_format=spec.v_fmt, hp=gpu_hp(t))
+        torch.cuda.synchronize()
+        for (_, off, m, _), d in zip(spec.offsets(), bufs):
+            assert torch.equal(d["param"].view(torch.int32), th_a[off:off + m].view(torch.int32))
+            for k in STATE_KEYS:
+                a = st_a[k]
+                ref = a[off:off + m] if k.endswith("codes") else a[off // G:(off + m) // G]
+                assert torch.equal(d[k].view(torch.uint8), ref.view(torch.uint8)), k
+        del g_a
