@@ -15,7 +15,11 @@ same shapes and plausible value distributions:
   scaled by 100 (the outlier channels of GLU-type models).
 
 Seeds: a tensor's parameters use ``1000 * config + index``; its gradient at
-step t uses that seed plus ``7919 * t``.  Generation runs on whichever device
+step t uses that seed plus ``7919 * t``.  The transcendental steps of the
+recipes (the log-normal scale, 10^U) run in float64 and are rounded once:
+torch's vectorized float32 exp and pow give different last bits on different
+x86 CPU generations, which would make the same seed draw different gradients
+on different hosts.  Generation runs on whichever device
 the caller names (a CPU generator for test-sized inputs, a device generator
 for the multi-gigabyte arenas); the two devices draw different streams, so a
 test always copies one side's generated tensor to the other.
@@ -127,8 +131,8 @@ def _tensor_scale(spec: ArenaSpec, idx: int, rows: int) -> torch.Tensor:
     Drawn once per tensor on the CPU so that every device agrees on it."""
     g = _gen(1000 * spec.config + 500 + idx, "cpu")
     if spec.grad_scale == "row":
-        return torch.randn(rows, generator=g).exp_()
-    return torch.randn(1, generator=g).exp_()
+        return torch.randn(rows, generator=g).double().exp().float()
+    return torch.randn(1, generator=g).double().exp().float()
 
 
 def gen_grads(spec: ArenaSpec, step: int, device="cpu", out: torch.Tensor | None = None,
@@ -145,7 +149,8 @@ def gen_grads(spec: ArenaSpec, step: int, device="cpu", out: torch.Tensor | None
             for c0 in range(0, n, chunk):
                 c1 = min(n, c0 + chunk)
                 m = c1 - c0
-                mag = torch.pow(10.0, torch.rand(m, generator=g, device=dev) * 10.0 - 8.0)
+                u = torch.rand(m, generator=g, device=dev).double()
+                mag = torch.pow(10.0, u * 10.0 - 8.0).float()
                 sign = torch.where(torch.rand(m, generator=g, device=dev) < 0.5, -1.0, 1.0)
                 zero = torch.rand(m, generator=g, device=dev) < 0.05
                 val = torch.where(zero, torch.zeros_like(mag), mag * sign)

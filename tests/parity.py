@@ -97,7 +97,7 @@ class StepResult(tuple):
     moments = None
     G = None
     v_fmt = None
-    grad_f32 = None
+    grad_bits = None
 
 
 def oracle_step(theta, g_bits, st, G, v_fmt, t, threads=THREADS):
@@ -109,31 +109,45 @@ def oracle_step(theta, g_bits, st, G, v_fmt, t, threads=THREADS):
                    G=G, v_fmt=v_fmt, hp=orc_hp(t), threads=threads, moments_out=(m_new, v_new))
     r = StepResult((th, s))
     r.moments, r.G, r.v_fmt = (m_new, v_new), G, v_fmt
-    r.grad_f32 = (g_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r.grad_bits = g_bits
     return r
+
+
+def _signed(c):
+    c = c.astype(np.int32)
+    return np.where(c & 0x80, -1, 1) * (c & 0x7F)
+
+
+def differing(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Indices where two code arrays differ, with 0x00 == 0x80 (byte ops only,
+    so that billion-element arenas stay cheap)."""
+    g, r = gpu.reshape(-1), ref.reshape(-1)
+    ne = g != r
+    ne &= ((g & 0x7F) != 0) | ((r & 0x7F) != 0)
+    return np.flatnonzero(ne)
 
 
 def code_diff(gpu: np.ndarray, ref: np.ndarray):
     """(fraction identical, max grid-step distance) with 0x00 == 0x80."""
-    g = gpu.astype(np.int32)
-    r = ref.astype(np.int32)
-    g = np.where((g & 0x7F) == 0, 0, g)
-    r = np.where((r & 0x7F) == 0, 0, r)
-    same = g == r
-    frac = float(same.mean()) if same.size else 1.0
-    if same.all():
-        return frac, 0
-    sg = np.where(g & 0x80, -1, 1) * (g & 0x7F)
-    sr = np.where(r & 0x80, -1, 1) * (r & 0x7F)
-    return frac, int(np.abs(sg - sr).max())
+    idx = differing(gpu, ref)
+    n = gpu.size
+    if idx.size == 0:
+        return 1.0, 0
+    g, r = gpu.reshape(-1)[idx], ref.reshape(-1)[idx]
+    return 1.0 - idx.size / n, int(np.abs(_signed(g) - _signed(r)).max())
 
 
-def assert_codes(gpu, ref, what, min_frac=CODE_MATCH_MIN, max_steps=1, record=True):
+def assert_codes(gpu, ref, what, min_frac=CODE_MATCH_MIN, max_steps=1, record=True, check=True):
+    """Identical codes (0x00 == 0x80) on at least min_frac of the elements and
+    no code more than max_steps grid steps away; check=False only records the
+    counts for the report."""
     frac, steps = code_diff(gpu, ref)
     n = gpu.size
     bad = int(round((1.0 - frac) * n))
     if record:
         STATS.append((what, n, bad, steps))
+    if not check:
+        return frac
     allowed = max(1, int((1.0 - min_frac) * n))
     assert bad <= allowed, f"{what}: {bad} of {n} codes differ ({frac:.6%} identical)"
     if max_steps is not None:
@@ -141,25 +155,27 @@ def assert_codes(gpu, ref, what, min_frac=CODE_MATCH_MIN, max_steps=1, record=Tr
     return frac
 
 
-def signed_steps(codes):
-    c = codes.astype(np.int32)
-    return np.where(c & 0x80, -1, 1) * (c & 0x7F)
-
-
-def assert_codes_given_k(gpu_codes, moments, gpu_k, fmt, G, what, cond=None, threads=THREADS):
-    """(B): the GPU's codes against the oracle's encoding of the oracle's own
-    moments with the GPU's stored k; cond (per element, or None for 1) is the
-    condition number bound of the moment update."""
+def assert_codes_given_k(gpu_codes, moments, gpu_k, fmt, G, what, cond=None, threads=THREADS,
+                         min_frac=CODE_MATCH_MIN):
+    # cond: None, or a function of element indices giving the condition bound there
+    """The GPU's codes against the oracle's encoding of the oracle's own
+    moments with the GPU's stored k: (A) at least min_frac identical, (B) every
+    code within its step bound -- one step, or for a first moment that is a
+    near-cancellation (cond: per-element condition number bound of the moment
+    update, None for 1) 1 + ceil(8 k 2^-21 cond / ln 2) steps."""
     want, _, _ = orc.expand_quantize_groups(fmt, moments, G, k_given=gpu_k, threads=threads)
-    dist = np.abs(signed_steps(gpu_codes) - signed_steps(want))
+    frac = assert_codes(gpu_codes, want, what + " (GPU k)", min_frac=min_frac, max_steps=None, record=False)
+    idx = differing(gpu_codes, want)
+    dist = np.abs(_signed(gpu_codes.reshape(-1)[idx]) - _signed(want.reshape(-1)[idx]))
     if cond is None:
-        allowed = 1
+        allowed = np.ones_like(dist)
     else:
-        k_el = np.repeat(gpu_k.astype(np.float64), G)
-        allowed = 1 + np.ceil(8.0 * k_el * 2.0 ** -21 * cond / math.log(2.0))
+        k_el = gpu_k.astype(np.float64)[idx // G]
+        allowed = 1 + np.ceil(8.0 * k_el * 2.0 ** -21 * cond(idx) / math.log(2.0))
     bad = dist > allowed
     assert not bad.any(), (f"{what} (GPU k): {int(bad.sum())} codes beyond their step bound; "
                            f"worst {int(dist[bad].max())} steps where {int(np.max(np.where(bad, allowed, 0)))} allowed")
+    return frac
 
 
 def assert_theta(gpu, ref, what):
@@ -180,15 +196,25 @@ def assert_amax(gpu, ref, amax_prev, what):
     assert not bad.any(), f"{what}: amax off in {int(bad.sum())} groups (worst {(d / np.maximum(ref, 1e-45)).max():.3e} rel)"
 
 
-def assert_k(gpu, ref, amax_ref, amax_prev, v_fmt_name, what):
+def k_conditioning(ref_k, amax_ref, amax_prev, v_fmt_name):
+    """Per group: (well, tol, ln_ratio).  k = ln R_fmt / ln(amax/amin) is
+    well-conditioned where the group range is at least 1.01 and the smallest
+    moment exceeds the FP32 rounding bound delta of the moment update; tol is
+    the relative bound on k there."""
     r_fmt = orc.fmt_max(v_fmt_name) / orc.fmt_min_subnormal(v_fmt_name)
-    ref = ref.astype(np.float64)
+    ref = ref_k.astype(np.float64)
     amax = amax_ref.astype(np.float64)
     ln_ratio = math.log(r_fmt) / ref                 # ln(amax / amin) from the stored k
     amin = amax * np.exp(-ln_ratio)
     delta = 2.0 ** -21 * (2 * np.abs(amax_prev.astype(np.float64)) + amax)
     well = (ln_ratio >= math.log(1.01)) & (delta < 0.5 * amin) & (amax > 0)
     tol = 1e-5 + 2.0 * (delta / np.where(amin > 0, amin, 1.0)) / ln_ratio
+    return well, tol
+
+
+def assert_k(gpu, ref, amax_ref, amax_prev, v_fmt_name, what):
+    well, tol = k_conditioning(ref, amax_ref, amax_prev, v_fmt_name)
+    ref = ref.astype(np.float64)
     rel = np.abs(gpu.astype(np.float64) - ref) / ref
     bad = well & (rel > tol)
     assert not bad.any(), f"{what}: k off by {rel[bad].max():.3e} relative in {int(bad.sum())} groups"
@@ -203,18 +229,33 @@ def assert_step_parity(gpu, ref, v_fmt, what, prev=None):
     prev_v = zeros if prev is None else prev["v_amax"]
     assert_theta(th_g, th_r, what + " theta")
     moments = getattr(ref, "moments", None)
-    # (A) against the oracle's codes; without the moments, also the one-step rule
-    step_rule = None if moments is not None else 1
-    fm = assert_codes(st_g["m_codes"], st_r["m_codes"], what + " m codes", max_steps=step_rule)
-    fv = assert_codes(st_g["v_codes"], st_r["v_codes"], what + " v codes", max_steps=step_rule)
-    if moments is not None:  # (B)
-        g_abs = np.abs(ref.grad_f32)
-        m_new = np.abs(moments[0].astype(np.float64))
-        terms = B1 * np.repeat(np.abs(prev_m.astype(np.float64)), ref.G) + (1.0 - B1) * g_abs
-        with np.errstate(divide="ignore", invalid="ignore"):
-            cond = np.where(m_new > 0, terms / m_new, np.inf)
-        assert_codes_given_k(st_g["m_codes"], moments[0], st_g["m_k"], "e4m3", ref.G, what + " m codes", cond=cond)
-        assert_codes_given_k(st_g["v_codes"], moments[1], st_g["v_k"], ref.v_fmt, ref.G, what + " v codes")
+    # Without the oracle's unquantized moments: identical codes on >= 99.99%,
+    # every mismatch one grid step.  With them, the codes are judged against
+    # the oracle's encoding of its own moments with the k the GPU stored beside
+    # them -- (A) >= 99.99% identical, (B) within the step bound -- because k is
+    # itself ill-conditioned wherever a group's smallest moment is a partial
+    # cancellation (any FP32 evaluation of the update moves it), and a whole
+    # group's codes then legitimately shift with it.  k is judged against the
+    # oracle's on its own, to its conditioning bound (assert_k); the mismatch
+    # count against the oracle's own codes is recorded for the report.
+    if moments is None:
+        fm = assert_codes(st_g["m_codes"], st_r["m_codes"], what + " m codes")
+        fv = assert_codes(st_g["v_codes"], st_r["v_codes"], what + " v codes")
+    else:
+        assert_codes(st_g["m_codes"], st_r["m_codes"], what + " m codes", check=False)
+        assert_codes(st_g["v_codes"], st_r["v_codes"], what + " v codes", check=False)
+        G = ref.G
+
+        def cond(idx):  # (b1 amax_prev + (1 - b1)|g|) / |m_new| at the given elements
+            g_abs = np.abs((ref.grad_bits[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+            m_new = np.abs(moments[0][idx].astype(np.float64))
+            terms = B1 * np.abs(prev_m[idx // G].astype(np.float64)) + (1.0 - B1) * g_abs
+            with np.errstate(divide="ignore", invalid="ignore"):
+                return np.where(m_new > 0, terms / m_new, np.inf)
+
+        fm = assert_codes_given_k(st_g["m_codes"], moments[0], st_g["m_k"], "e4m3", ref.G, what + " m codes",
+                                  cond=cond)
+        fv = assert_codes_given_k(st_g["v_codes"], moments[1], st_g["v_k"], ref.v_fmt, ref.G, what + " v codes")
     assert_amax(st_g["m_amax"], st_r["m_amax"], prev_m, what + " m amax")
     assert_amax(st_g["v_amax"], st_r["v_amax"], prev_v, what + " v amax")
     assert_k(st_g["m_k"], st_r["m_k"], st_r["m_amax"], prev_m, "e4m3", what + " m k")
