@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a
     __shared__ float2 tab[512];
     fill_tab(tab, a.p);
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) +
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (chunk >= a.n_chunks) return;
     if (chunk < a.buf.n / kWaveElems)  // every lane in range
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fp8_step_list_kernel(const StepL
     __shared__ float2 tab[512];
     fill_tab(tab, a.p);
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) +
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (chunk >= a.total_chunks) return;
     int lo = 0, hi = a.n_tensors;  // chunk_start[lo] <= chunk < chunk_start[hi]

@@ -3,7 +3,7 @@
 //
 // step_skeleton moves exactly the bytes of the fused FP8-state AdamW step, with
 // the same launch shape (one 1024-parameter chunk per wave, 256-thread
-// workgroups) and the same per-lane layout (16 consecutive parameters: 64 B of
+// workgroups, the same XCD-aware workgroup order) and the same per-lane layout (16 consecutive parameters: 64 B of
 // FP32 master weights, 32 B of BF16 gradient, 16 B of each FP8 moment, the
 // group's (amax, k) of both moments), but replaces the arithmetic with a
 // trivial dependence on every loaded byte.  copy_stream is a plain 16-byte-
@@ -25,9 +25,18 @@ struct SkelArgs {
     int64_t n_chunks;
 };
 
+// The step's XCD-aware workgroup order: the dispatcher deals workgroups to the
+// eight XCDs round-robin; each XCD sweeps runs of 256 consecutive logical
+// workgroups (blocks past the last whole run of 8 x 256 keep their index).
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t nb) {
+    if (b >= nb / 2048 * 2048) return b;
+    const int64_t q = b >> 3;
+    return (q / 256) * 2048 + (b & 7) * 256 + q % 256;
+}
+
 __global__ __launch_bounds__(256) void step_skeleton(SkelArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t c = xcd_order(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     if (c >= a.n_chunks) return;
     const int64_t base = c * 1024;
     f4 *tp = reinterpret_cast<f4 *>(a.param + base) + lane * 4;

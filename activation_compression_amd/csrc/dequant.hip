@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kBlock) void dequant_per_tensor_kernel(const uint8_
                                                                     uint16_t *__restrict__ out) {
     const float scale = *scale_p;
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= n_chunks) return;
     const int64_t e0 = chunk * kWaveElems + lane * 16;
     if (e0 + 16 <= n) {
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void dequant_group_kernel(const uint8_t *__
                                                                int64_t n_chunks, const float *__restrict__ scales,
                                                                uint16_t *__restrict__ out) {
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= n_chunks) return;
     const int64_t e0 = chunk * kWaveElems + lane * 16;
     if (e0 >= n) return;  // n % G == 0 and G >= 32: lanes are all in or all out

@@ -66,6 +66,26 @@ __device__ __forceinline__ v2f decode2_e4m3(uint32_t w) {
     return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
 }
 
+// ---- XCD-aware block order.  The dispatcher deals workgroups to the eight
+// XCDs round-robin (workgroup b runs on XCD b % 8), so in launch order the
+// XCDs interleave at single-workgroup granularity.  Streaming kernels remap
+// the workgroup index so that each XCD sweeps runs of kXcdRun consecutive
+// logical workgroups instead: XCD x takes logical blocks [s*8R + x*R,
+// s*8R + (x+1)*R) of super-run s.  Blocks past the last whole super-run keep
+// their index.  A bijection on [0, nblocks).  Measured on MI355X: a
+// memory-only model of the optimizer step 5.19 -> 5.32 TB/s with R = 256
+// (32 .. 8192 all gained, 256 most); the 1xG cast 4%, the dequantization 2%
+// faster; the optimizer step itself and SwiGLU unchanged.  The row-per-wave
+// RMSNorm and the read-only stage-1 pass lost 1-7% and keep the launch order.
+constexpr int64_t kXcdRun = 256;
+
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nblocks) {
+    constexpr int64_t W = 8 * kXcdRun;
+    if (b >= nblocks / W * W) return b;
+    const int64_t q = b >> 3;
+    return (q / kXcdRun) * W + (b & 7) * kXcdRun + q % kXcdRun;
+}
+
 // ---- bit helpers
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

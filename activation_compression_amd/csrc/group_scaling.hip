@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void quant_per_tensor_kernel(const uint16_t
     const CastQ q = cast_q(A);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = A > 0.0f ? A / 448.0f : 1.0f;
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
     if (chunk < n_chunks) {
         const int64_t e0 = chunk * kWaveElems + lane * 16;
         if (e0 + 16 <= n) {
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void quant_group_kernel(const uint16_t *__r
                                                              float *__restrict__ partial) {
     constexpr int LPG = G / 16;
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
     if (chunk < n_chunks) {
         const int64_t e0 = chunk * kWaveElems + lane * 16;
         const bool act = e0 < n;

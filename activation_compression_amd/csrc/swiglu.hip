@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_fused_kernel(const uint16_t *__
                                                               float *__restrict__ up_scales) {
     constexpr int LPG = G / 16;
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= n_chunks) return;
     const int64_t e0 = chunk * kWaveElems + lane * 16;
     const bool act = e0 < n;  // n % G == 0, G >= 32: a lane is all in or all out
