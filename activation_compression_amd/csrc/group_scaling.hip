@@ -56,10 +56,15 @@ __global__ __launch_bounds__(kBlock) void absmax_stage1_kernel(const uint16_t *_
 __global__ __launch_bounds__(kBlock) void absmax_stage2_kernel(const float *__restrict__ partial, int64_t n,
                                                                float *__restrict__ amax) {
     __shared__ uint32_t red[kBlock / 64];
-    uint32_t m = 0u;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
-        m = max(m, __float_as_uint(partial[i]) & 0x7FFFFFFFu);
+    int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // eight loads in flight per thread
+    for (; i + 7 * stride < n; i += 8 * stride) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = max(acc[j], __float_as_uint(partial[i + j * stride]) & 0x7FFFFFFFu);
+    }
+    for (; i < n; i += stride) acc[0] = max(acc[0], __float_as_uint(partial[i]) & 0x7FFFFFFFu);
+    uint32_t m = max(max(max(acc[0], acc[1]), max(acc[2], acc[3])), max(max(acc[4], acc[5]), max(acc[6], acc[7])));
     m = run_max<64>(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
@@ -67,7 +72,10 @@ __global__ __launch_bounds__(kBlock) void absmax_stage2_kernel(const float *__re
         uint32_t b = red[0];
 #pragma unroll
         for (int i = 1; i < kBlock / 64; ++i) b = max(b, red[i]);
-        if (b != 0u) atomicMax(reinterpret_cast<unsigned int *>(amax), b);
+        // Atomics on one address serialize in L2: skip those that cannot raise
+        // the value.  The load may be stale, which only costs an atomic.
+        unsigned int *dst = reinterpret_cast<unsigned int *>(amax);
+        if (b > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(dst, b);
     }
 }
 
@@ -155,9 +163,10 @@ hipError_t launch_qg(const uint16_t *x, int64_t n, int64_t nc, uint8_t *codes, f
     return launch_k(k, chunk_grid<k>(nc, num_cus), s, x, n, nc, codes, scales, partial);
 }
 
+// About 32 partials per thread: few workgroups, so few atomics on the target.
 hipError_t launch_stage2(const float *partial, int64_t n, float *amax, hipStream_t s, int num_cus) {
     constexpr auto k = &absmax_stage2_kernel;
-    return launch_k(k, resident_grid<k>(ceil_div(n, (int64_t)kBlock * 4), num_cus), s, partial, n, amax);
+    return launch_k(k, resident_grid<k>(ceil_div(n, (int64_t)kBlock * 32), num_cus), s, partial, n, amax);
 }
 
 }  // namespace
