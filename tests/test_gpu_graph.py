@@ -1,0 +1,139 @@
+"""The hot path captured into a HIP graph and replayed.
+
+No entry point allocates, synchronizes or enqueues a memset: every buffer is
+the caller's, per-tensor statistics stay on the device, and stage 1 clears
+the stage-2 target with a kernel of its own.  So the whole activation path
+and the optimizer step (arena and tensor-list forms) can be captured once
+and replayed; each replay must reproduce the eager result bit for bit.  Each
+test replays several times with new inputs written eagerly in between and
+the outputs clobbered before the eager reference run."""
+import numpy as np
+import pytest
+import torch
+
+from activation_compression_amd import coat, inputs
+from parity import flush, gpu_hp
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+G = 128
+
+
+def capture(fn):
+    """Warm up on a side stream (caches device queries), then capture fn."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def act_bits(rows, cols, seed):
+    spec = inputs.ActivationSpec(f"g{rows}x{cols}", rows, cols, seed=seed)
+    return inputs.gen_activation(spec, device="cuda")
+
+
+def test_activation_path_graph_replays():
+    rows, cols, wide = 256, 4096, 1024 * 3
+    x = torch.empty((rows, cols), dtype=torch.int16, device="cuda")
+    gate = torch.empty((rows, wide), dtype=torch.int16, device="cuda")
+    up = torch.empty_like(gate)
+    w = inputs.gen_norm_weight(cols, device="cuda")
+    n, nw = rows * cols, rows * wide
+    f32 = lambda m: torch.empty(m, device="cuda")
+    u8 = lambda m: torch.empty(m, dtype=torch.uint8, device="cuda")
+    i16 = lambda m: torch.empty(m, dtype=torch.int16, device="cuda")
+    out = dict(partial=f32(n // G), amax=f32(1), codes=u8(n), scale=f32(1), gcodes=u8(n), gscales=f32(n // G),
+               gpartial=f32(n // G), h=i16(nw), hp=f32(nw // G), hamax=f32(1), hcodes=u8(nw), hscale=f32(1),
+               gc=u8(nw), gs=f32(nw // G), uc=u8(nw), us=f32(nw // G), y=i16(n), yp=f32(n // G), rstd=f32(rows),
+               xc=u8(n), xs=f32(n // G), deq=i16(n))
+    o = out
+
+    def path():
+        coat.coat_group_absmax(x, o["partial"], o["amax"], group_size=G)
+        coat.coat_quant_per_tensor(x, o["amax"], o["codes"], o["scale"])
+        coat.coat_quant_group(x, o["gcodes"], o["gscales"], o["gpartial"], group_size=G)
+        coat.coat_swiglu_fused(gate, up, o["h"], o["hp"], (o["gc"], o["gs"], o["uc"], o["us"]), group_size=G)
+        coat.coat_absmax_reduce(o["hp"], o["hamax"])
+        coat.coat_quant_per_tensor(o["h"], o["hamax"], o["hcodes"], o["hscale"])
+        coat.coat_rmsnorm_fused(x, w, o["y"], o["yp"], o["rstd"], (o["xc"], o["xs"]), group_size=G)
+        coat.coat_dequant_group(o["gcodes"], o["gscales"], o["deq"], rows=rows, cols=cols, group_size=G)
+
+    x.copy_(act_bits(rows, cols, 90))
+    gate.copy_(act_bits(rows, wide, 91))
+    up.copy_(act_bits(rows, wide, 92))
+    graph = capture(path)
+    for trial in range(3):
+        x.copy_(act_bits(rows, cols, 100 + trial))
+        gate.copy_(act_bits(rows, wide, 200 + trial))
+        up.copy_(act_bits(rows, wide, 300 + trial))
+        flush(f"activation graph replay {trial}")
+        graph.replay()
+        torch.cuda.synchronize()
+        snap = {k: v.clone() for k, v in o.items()}
+        for v in o.values():
+            v.view(torch.uint8).fill_(0x5A)
+        path()
+        torch.cuda.synchronize()
+        for k in o:
+            assert torch.equal(snap[k].view(torch.uint8), o[k].view(torch.uint8)), f"replay {trial}: {k}"
+
+
+@pytest.mark.parametrize("form", ["arena", "list"])
+def test_optimizer_step_graph_replays(form):
+    """Step t = 3 captured with its hyper-parameters; every replay starts from
+    the same restored state and must equal an eager step from that state."""
+    spec = inputs.ragged_list(G, "e4m3")
+    n = spec.numel
+    theta0 = inputs.gen_params(spec, device="cuda")
+    st0 = inputs.fresh_state(n, G, device="cuda")
+    # a non-trivial starting state: two eager steps from fresh
+    for t in (1, 2):
+        g = inputs.gen_grads(spec, t, device="cuda")
+        coat.coat_adamw_step(theta0, g, st0["m_codes"], st0["m_amax"], st0["m_k"], st0["v_codes"],
+                             st0["v_amax"], st0["v_k"], group_size=G, v_format="e4m3", hp=gpu_hp(t))
+    theta = theta0.clone()
+    grad = torch.empty(n, dtype=torch.int16, device="cuda")
+    st = {k: v.clone() for k, v in st0.items()}
+    keys = ("m_codes", "m_amax", "m_k", "v_codes", "v_amax", "v_k")
+    if form == "list":
+        bufs = []
+        for _, off, m, _ in spec.offsets():
+            d = {"param": theta[off:off + m], "grad": grad[off:off + m]}
+            for k in keys:
+                d[k] = st[k][off:off + m] if k.endswith("codes") else st[k][off // G:(off + m) // G]
+            bufs.append(d)
+        table = coat.AdamWTensorList(bufs, group_size=G)
+        step = lambda: coat.coat_adamw_step_list(table, v_format="e4m3", hp=gpu_hp(3))
+    else:
+        step = lambda: coat.coat_adamw_step(theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"],
+                                            st["v_amax"], st["v_k"], group_size=G, v_format="e4m3", hp=gpu_hp(3))
+
+    def restore():
+        theta.copy_(theta0)
+        for k in keys:
+            st[k].copy_(st0[k])
+
+    grad.copy_(inputs.gen_grads(spec, 3, device="cuda"))
+    restore()
+    graph = capture(step)
+    for trial in range(3):
+        grad.copy_(inputs.gen_grads(spec, 3 + trial, device="cuda"))
+        restore()
+        flush(f"{form} step graph replay {trial}")
+        graph.replay()
+        torch.cuda.synchronize()
+        snap = [theta.clone()] + [st[k].clone() for k in keys]
+        restore()
+        step()
+        torch.cuda.synchronize()
+        now = [theta] + [st[k] for k in keys]
+        for a, b, name in zip(snap, now, ("param",) + keys):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {trial}: {name}"
