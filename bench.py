@@ -246,6 +246,9 @@ def cpu_baseline(spec, acts, G, threads):
     args = lambda: (theta, None, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"], st["v_k"])
     a = list(args()); a[1] = g1
     orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(1), threads=threads)
+    m1 = 8 << 20  # the single-thread sample: the first 8 Mi parameters, same step 2
+    th1 = theta[:m1].copy()
+    st1 = {k: (v[:m1].copy() if k.endswith("codes") else v[:m1 // G].copy()) for k, v in st.items()}
     a = list(args()); a[1] = g2
     t0 = time.perf_counter()
     orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(2), threads=threads)
@@ -262,14 +265,21 @@ def cpu_baseline(spec, acts, G, threads):
         orc.quant_group(x, G, threads=threads)
         t_act += (time.perf_counter() - t0) * act.rows / rows
     total = t_step + t_act
+
+    t0 = time.perf_counter()
+    orc.adamw_step(th1, g2[:m1], st1["m_codes"], st1["m_amax"], st1["m_k"], st1["v_codes"], st1["v_amax"],
+                   st1["v_k"], G=G, v_fmt=spec.v_fmt, hp=hp(2), threads=1)
+    single = m1 / (time.perf_counter() - t0)
     return {
         "value": spec.numel / total,
         "unit": "params/s",
         "cores": threads,
         "kind": "oracle",
+        "single_thread_step_params_per_s": single,
         "sample": (f"AdamW step 2 on the first {n_tensors} tensors of the arena ({n} params, scaled x"
                    f"{spec.numel / n:.1f}); Group Scaling + casts on the first {rows} rows of each "
-                   f"activation tensor (scaled); binary64 C oracle, {threads} threads"),
+                   f"activation tensor (scaled); binary64 C oracle, {threads} threads; the single-thread "
+                   f"rate is the same step on the first {m1} params"),
         "seconds_per_step": total,
     }
 
@@ -416,6 +426,7 @@ def main():
             "device_ceiling": ceiling,
         },
         "cpu_baseline": cpu,
+        "gpu_over_cpu_baseline": None if cpu is None else round(n / (ms_per_step * 1e-3) / cpu["value"], 1),
         "kernels": kernels,
         "extras": extra,
         "step_hbm_gb_per_s": round(sum(alg.values()) / (ms_per_step * 1e-3) / 1e9, 1),

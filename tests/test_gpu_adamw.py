@@ -55,6 +55,35 @@ def test_ten_steps_along_the_oracle_trajectory(v_fmt):
     flush(f"identical code fraction per step (m, v): {fracs}")
 
 
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_ten_steps_free_running(v_fmt):
+    """Config 1, ten steps, each side alone: the GPU keeps its own state on the
+    device, the oracle its own.  Once a code flips the two trajectories may
+    part by more than the per-step tolerance, so this is a sanity bound on
+    the drift: median theta relative difference <= 1e-6, the 99.99th
+    percentile <= 1e-3, and the final codes still overwhelmingly identical."""
+    spec, theta, grads = config1_inputs(10)
+    G = 128
+    th_d = dev(theta)
+    st_d = {k: dev(v) for k, v in np_state(spec.numel, G).items()}
+    th_r, st_r = theta, np_state(spec.numel, G)
+    for t in range(1, 11):
+        coat.coat_adamw_step(th_d, dev(grads[t - 1]), st_d["m_codes"], st_d["m_amax"], st_d["m_k"], st_d["v_codes"],
+                             st_d["v_amax"], st_d["v_k"], group_size=G, v_format=v_fmt, hp=gpu_hp(t))
+        th_r, st_r = oracle_step(th_r, grads[t - 1], st_r, G, v_fmt, t)
+    torch.cuda.synchronize()
+    th_g = host(th_d).astype(np.float64)
+    ref = th_r.astype(np.float64)
+    rel = np.abs(th_g - ref) / np.maximum(np.abs(ref), 1e-3 * LR)
+    med, p9999 = float(np.median(rel)), float(np.percentile(rel, 99.99))
+    same_m = float((host(st_d["m_codes"]) == st_r["m_codes"]).mean())
+    same_v = float((host(st_d["v_codes"]) == st_r["v_codes"]).mean())
+    flush(f"free-running 10 steps v={v_fmt}: theta rel median {med:.2e}, 99.99% {p9999:.2e}; "
+          f"identical codes m {same_m:.6f} v {same_v:.6f}")
+    assert med <= 1e-6 and p9999 <= 1e-3
+    assert same_m >= 0.999 and same_v >= 0.999
+
+
 def stress_inputs(n, G, v_fmt, steps=2):
     spec = inputs.stress(G, v_fmt, numel=n)
     theta = inputs.gen_params(spec).numpy()
