@@ -206,35 +206,33 @@ def _arena_step(th_d, g_d, st_d, spec, t):
 
 
 @pytest.mark.slow
-def test_olmo1b_shaped_arena_two_steps_in_full():
+def test_olmo1b_shaped_arena_five_steps_in_full():
     """The whole OLMo-1B-shaped arena (1 176 764 416 params, v in E5M2) in one
-    launch, every element compared, two steps: step 2 starts from the
-    oracle's step-1 state copied onto the device."""
+    launch, every element compared, five steps in lockstep: step t starts on
+    both sides from the oracle's state after step t-1, copied onto the
+    device."""
     spec = inputs.olmo_1b()
     G, n = spec.group_size, spec.numel
     flush(f"generating {spec.name}")
     th_d = inputs.gen_params(spec, device="cuda")
-    g1_d = inputs.gen_grads(spec, 1, device="cuda")
-    g2_d = inputs.gen_grads(spec, 2, device="cuda")
     st_d = inputs.fresh_state(n, G, device="cuda")
-    theta0, g1, g2 = host(th_d), host(g1_d), host(g2_d)
-    st0 = np_state(n, G)
-    flush("GPU step 1")
-    _arena_step(th_d, g1_d, st_d, spec, 1)
-    gpu1 = (host(th_d), {k: host(v) for k, v in st_d.items()})
-    flush("oracle step 1")
-    ref1 = oracle_step(theta0, g1, st0, G, spec.v_fmt, 1, threads=_threads())
-    assert_step_parity(gpu1, ref1, spec.v_fmt, "olmo-1b step 1")
-    del gpu1
-    flush("GPU step 2 from the oracle's state")
-    th_d.copy_(torch.from_numpy(ref1[0]))
-    for k, v in ref1[1].items():
-        st_d[k].copy_(torch.from_numpy(v))
-    _arena_step(th_d, g2_d, st_d, spec, 2)
-    gpu2 = (host(th_d), {k: host(v) for k, v in st_d.items()})
-    flush("oracle step 2")
-    ref2 = oracle_step(ref1[0], g2, ref1[1], G, spec.v_fmt, 2, threads=_threads())
-    assert_step_parity(gpu2, ref2, spec.v_fmt, "olmo-1b step 2", prev=ref1[1])
+    theta, st = host(th_d), np_state(n, G)
+    for t in range(1, 6):
+        g_d = inputs.gen_grads(spec, t, device="cuda")
+        g = host(g_d)
+        if t > 1:
+            th_d.copy_(torch.from_numpy(theta))
+            for k, v in st.items():
+                st_d[k].copy_(torch.from_numpy(v))
+        flush(f"GPU step {t}")
+        _arena_step(th_d, g_d, st_d, spec, t)
+        gpu = (host(th_d), {k: host(v) for k, v in st_d.items()})
+        del g_d
+        flush(f"oracle step {t}")
+        ref = oracle_step(theta, g, st, G, spec.v_fmt, t, threads=_threads())
+        assert_step_parity(gpu, ref, spec.v_fmt, f"olmo-1b step {t}", prev=None if t == 1 else st)
+        del gpu
+        theta, st = ref
 
 
 @pytest.mark.slow
@@ -446,3 +444,37 @@ def test_olmo1b_shaped_tensor_list_bitwise_vs_arena():
                 ref = a[off:off + m] if k.endswith("codes") else a[off // G:(off + m) // G]
                 assert torch.equal(d[k].view(torch.uint8), ref.view(torch.uint8)), k
         del g_a
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_checkpoint_resume_bit_identical(v_fmt):
+    """The optimizer state is exactly theta, the m/v codes, each group's
+    (amax, k) and the step count: saved to host memory after step 2 and
+    restored into fresh device buffers, two more steps give the same bytes as
+    four uninterrupted steps."""
+    spec, theta, grads = config1_inputs(4)
+    G = 128
+
+    def run(th_d, st_d, steps):
+        for t in steps:
+            coat.coat_adamw_step(th_d, dev(grads[t - 1]), st_d["m_codes"], st_d["m_amax"], st_d["m_k"],
+                                 st_d["v_codes"], st_d["v_amax"], st_d["v_k"], group_size=G, v_format=v_fmt,
+                                 hp=gpu_hp(t))
+        torch.cuda.synchronize()
+
+    th_a = dev(theta)
+    st_a = {k: dev(v) for k, v in np_state(spec.numel, G).items()}
+    run(th_a, st_a, (1, 2, 3, 4))
+
+    th_b = dev(theta)
+    st_b = {k: dev(v) for k, v in np_state(spec.numel, G).items()}
+    run(th_b, st_b, (1, 2))
+    ckpt = {"theta": host(th_b).copy(), "step": 2, **{k: host(v).copy() for k, v in st_b.items()}}
+    del th_b, st_b
+    torch.cuda.empty_cache()
+    th_c = dev(ckpt["theta"])
+    st_c = {k: dev(ckpt[k]) for k in st_a}
+    run(th_c, st_c, (ckpt["step"] + 1, ckpt["step"] + 2))
+    assert (host(th_c).view(np.uint32) == host(th_a).view(np.uint32)).all()
+    for k in st_a:
+        assert (host(st_c[k]).view(np.uint8) == host(st_a[k]).view(np.uint8)).all(), k
