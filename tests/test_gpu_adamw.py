@@ -57,31 +57,44 @@ def test_ten_steps_along_the_oracle_trajectory(v_fmt):
 
 @pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
 def test_ten_steps_free_running(v_fmt):
-    """Config 1, ten steps, each side alone: the GPU keeps its own state on the
-    device, the oracle its own.  Once a code flips the two trajectories may
-    part by more than the per-step tolerance, so this is a sanity bound on
-    the drift: median theta relative difference <= 1e-6, the 99.99th
-    percentile <= 1e-3, and the final codes still overwhelmingly identical."""
+    """Config 1, ten steps, the GPU keeping its own state on the device.
+
+    Two FP8-state trajectories that differ by one FP32 rounding do not stay
+    close: k is set by each group's smallest moment, a near-cancellation, and
+    a change of k moves whole groups' codes, which feeds the next step's
+    smallest moments (measured: the k difference between the GPU's and the
+    oracle's free-running trajectories grows about tenfold per step, 6e-8
+    after step 1).  So the free-running trajectory is judged two ways:
+    * every step is exact to the parity bar against the oracle's step taken
+      from the GPU's own state (lockstep anchored on the GPU);
+    * after ten steps it is as close to unquantized binary64 AdamW as the
+      oracle's own free-running trajectory is (median and 99.9th percentile
+      of |theta - theta_f64| within 1.25x and 1.5x of the oracle's)."""
     spec, theta, grads = config1_inputs(10)
     G = 128
     th_d = dev(theta)
     st_d = {k: dev(v) for k, v in np_state(spec.numel, G).items()}
     th_r, st_r = theta, np_state(spec.numel, G)
+    th64, m64, v64 = theta.astype(np.float64), np.zeros(spec.numel), np.zeros(spec.numel)
     for t in range(1, 11):
-        coat.coat_adamw_step(th_d, dev(grads[t - 1]), st_d["m_codes"], st_d["m_amax"], st_d["m_k"], st_d["v_codes"],
+        g = grads[t - 1]
+        th_in, st_in = host(th_d), {k: host(v) for k, v in st_d.items()}
+        anchored = oracle_step(th_in, g, st_in, G, v_fmt, t)
+        coat.coat_adamw_step(th_d, dev(g), st_d["m_codes"], st_d["m_amax"], st_d["m_k"], st_d["v_codes"],
                              st_d["v_amax"], st_d["v_k"], group_size=G, v_format=v_fmt, hp=gpu_hp(t))
-        th_r, st_r = oracle_step(th_r, grads[t - 1], st_r, G, v_fmt, t)
-    torch.cuda.synchronize()
-    th_g = host(th_d).astype(np.float64)
-    ref = th_r.astype(np.float64)
-    rel = np.abs(th_g - ref) / np.maximum(np.abs(ref), 1e-3 * LR)
-    med, p9999 = float(np.median(rel)), float(np.percentile(rel, 99.99))
-    same_m = float((host(st_d["m_codes"]) == st_r["m_codes"]).mean())
-    same_v = float((host(st_d["v_codes"]) == st_r["v_codes"]).mean())
-    flush(f"free-running 10 steps v={v_fmt}: theta rel median {med:.2e}, 99.99% {p9999:.2e}; "
-          f"identical codes m {same_m:.6f} v {same_v:.6f}")
-    assert med <= 1e-6 and p9999 <= 1e-3
-    assert same_m >= 0.999 and same_v >= 0.999
+        torch.cuda.synchronize()
+        gpu = (host(th_d), {k: host(v) for k, v in st_d.items()})
+        assert_step_parity(gpu, anchored, v_fmt, f"free-running step {t}", prev=st_in)
+        th_r, st_r = oracle_step(th_r, g, st_r, G, v_fmt, t)
+        orc.adamw_step_f64(th64, (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64), m64, v64,
+                           orc_hp(t))
+    e_gpu = np.abs(host(th_d).astype(np.float64) - th64)
+    e_orc = np.abs(th_r.astype(np.float64) - th64)
+    q = lambda e, p: float(np.quantile(e, p))
+    flush(f"free-running 10 steps v={v_fmt}: |theta - theta_f64| median gpu {q(e_gpu, .5):.3e} oracle "
+          f"{q(e_orc, .5):.3e}; 99.9% gpu {q(e_gpu, .999):.3e} oracle {q(e_orc, .999):.3e}")
+    assert q(e_gpu, 0.5) <= 1.25 * q(e_orc, 0.5)
+    assert q(e_gpu, 0.999) <= 1.5 * q(e_orc, 0.999)
 
 
 def stress_inputs(n, G, v_fmt, steps=2):
