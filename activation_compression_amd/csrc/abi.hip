@@ -18,6 +18,11 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_group(int32_t G) { return G >= 32 && G <= 1024 && (G & (G - 1)) == 0; }
 
+// Streaming launches give each 256-thread workgroup 4096 elements; the grid's
+// x dimension must stay below 2^31.
+constexpr int64_t kMaxElems = (int64_t)0x7FFFFFFF * coat::kWaveElems * (coat::kBlock / 64);
+bool fits_grid(int64_t n) { return n <= kMaxElems; }
+
 // Compute units of the current device, looked up once per device.
 int num_cus() {
     static std::atomic<int> cache[64];
@@ -91,7 +96,7 @@ coat_status check_bufs(const coat::StepBufs &b, int32_t group_size) {
         (b.param_bf16 && !aligned(b.param_bf16, 16)))
         return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (b.n <= 0 || b.n % group_size != 0) return COAT_ERR_SHAPE;
+    if (b.n <= 0 || b.n % group_size != 0 || !fits_grid(b.n)) return COAT_ERR_SHAPE;
     return COAT_OK;
 }
 
@@ -160,7 +165,8 @@ coat_status coat_group_absmax(const uint16_t *x_bf16, int64_t rows, int64_t cols
     if (!x_bf16 || !partial_amax || !amax) return COAT_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(partial_amax, 4) || !aligned(amax, 4)) return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols || !fits_grid(rows * cols))
+        return COAT_ERR_SHAPE;
     return from_hip(coat::launch_group_absmax(x_bf16, rows * cols, group_size, partial_amax, amax,
                                               (hipStream_t)stream, num_cus()));
 }
@@ -177,7 +183,7 @@ coat_status coat_quant_per_tensor(const uint16_t *x_bf16, int64_t n, const float
     if (!x_bf16 || !amax || !codes || !scale) return COAT_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(amax, 4) || !aligned(scale, 4))
         return COAT_ERR_ALIGN;
-    if (n <= 0 || n % 8 != 0) return COAT_ERR_SHAPE;
+    if (n <= 0 || n % 8 != 0 || !fits_grid(n)) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_quant_per_tensor(x_bf16, n, amax, codes, scale, (hipStream_t)stream,
                                                   num_cus()));
 }
@@ -189,7 +195,8 @@ coat_status coat_quant_group(const uint16_t *x_bf16, int64_t rows, int64_t cols,
         (partial_amax_or_null && !aligned(partial_amax_or_null, 4)))
         return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols || !fits_grid(rows * cols))
+        return COAT_ERR_SHAPE;
     return from_hip(coat::launch_quant_group(x_bf16, rows * cols, group_size, codes, scales,
                                              partial_amax_or_null, (hipStream_t)stream, num_cus()));
 }
@@ -198,7 +205,7 @@ coat_status coat_dequant_per_tensor(const uint8_t *codes, int64_t n, const float
                                     void *stream) {
     if (!codes || !scale || !out_bf16) return COAT_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scale, 4)) return COAT_ERR_ALIGN;
-    if (n <= 0 || n % 8 != 0) return COAT_ERR_SHAPE;
+    if (n <= 0 || n % 8 != 0 || !fits_grid(n)) return COAT_ERR_SHAPE;
     return from_hip(coat::launch_dequant_per_tensor(codes, n, scale, out_bf16, (hipStream_t)stream));
 }
 
@@ -207,7 +214,8 @@ coat_status coat_dequant_group(const uint8_t *codes, int64_t rows, int64_t cols,
     if (!codes || !scales || !out_bf16) return COAT_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales, 4)) return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols || !fits_grid(rows * cols))
+        return COAT_ERR_SHAPE;
     return from_hip(coat::launch_dequant_group(codes, rows * cols, group_size, scales, out_bf16,
                                                (hipStream_t)stream));
 }
@@ -223,7 +231,8 @@ coat_status coat_swiglu_fused(const uint16_t *gate_bf16, const uint16_t *up_bf16
                    !aligned(up_scales, 4))))
         return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols) return COAT_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || rows > INT64_MAX / cols || !fits_grid(rows * cols))
+        return COAT_ERR_SHAPE;
     return from_hip(coat::launch_swiglu_fused(gate_bf16, up_bf16, rows * cols, group_size, h_bf16, h_partial_amax,
                                               gate_codes, gate_scales, up_codes, up_scales, (hipStream_t)stream));
 }
@@ -238,7 +247,9 @@ coat_status coat_rmsnorm_fused(const uint16_t *x_bf16, const uint16_t *weight_bf
         (x_codes && (!aligned(x_codes, 16) || !aligned(x_scales, 4))))
         return COAT_ERR_ALIGN;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
-    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || cols > coat::kRmsNormMaxCols) return COAT_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % group_size != 0 || cols > coat::kRmsNormMaxCols ||
+        rows > (int64_t)0x7FFFFFFF * (coat::kBlock / 64))
+        return COAT_ERR_SHAPE;
     if (!(eps > 0.0f) || !(eps < INFINITY)) return COAT_ERR_HPARAM;
     return from_hip(coat::launch_rmsnorm_fused(x_bf16, weight_bf16, rows, (int)cols, group_size, eps, y_bf16,
                                                y_partial_amax, rstd, x_codes, x_scales, (hipStream_t)stream));
@@ -254,11 +265,14 @@ coat_status coat_adamw_list_pack(const coat_adamw_tensor *tensors, int32_t n_ten
     if (!tensors || !table_host) return COAT_ERR_NULL;
     if (n_tensors <= 0) return COAT_ERR_SHAPE;
     if (!valid_group(group_size)) return COAT_ERR_GROUP;
+    int64_t chunks = 0;
     const bool bf16 = tensors[0].param_bf16 != nullptr;
     for (int32_t t = 0; t < n_tensors; ++t) {
         const coat_status s = check_bufs(to_bufs(tensors[t]), group_size);
         if (s != COAT_OK) return s;
         if ((tensors[t].param_bf16 != nullptr) != bf16) return COAT_ERR_NULL;
+        chunks += coat::ceil_div(tensors[t].n, coat::kWaveElems);
+        if (!fits_grid(chunks * coat::kWaveElems)) return COAT_ERR_SHAPE;
     }
     unsigned char *out = static_cast<unsigned char *>(table_host);
     unsigned char *starts = out + sizeof(ListHeader);

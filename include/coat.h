@@ -33,6 +33,8 @@
  *   axis, never across tokens); the optimizer groups are consecutive runs of
  *   the flat parameter arena, so a tensor whose size is a multiple of G never
  *   shares a group with its neighbour.
+ * - Sizes: one launch covers at most (2^31 - 1) * 4096 elements (about
+ *   8.8e12; the launch grid's limit); larger sizes return COAT_ERR_SHAPE.
  * - NaN or infinite inputs are outside the contract.
  */
 #ifndef COAT_H

@@ -231,3 +231,20 @@ def test_step_list_validates_before_launch():
     assert L.coat_adamw_step_list(host, devp, 0, ctypes.byref(bad), None) == 6
     junk = np.zeros_like(buf)
     assert L.coat_adamw_step_list(ctypes.c_void_p(junk.ctypes.data), devp, 0, ctypes.byref(hp), None) == 3
+
+
+def test_sizes_beyond_the_launch_grid_are_rejected(L):
+    """(2^31 - 1) * 4096 elements is the most one launch covers; validation
+    rejects more before anything is enqueued."""
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    big = (2 ** 31) * 4096
+    assert L.coat_quant_per_tensor(f, big, f, f, f, None) == 3
+    assert L.coat_quant_group(f, big // 4096, 4096, 128, f, f, None, None) == 3
+    assert L.coat_dequant_per_tensor(f, big, f, f, None) == 3
+    from activation_compression_amd import coat
+    hp = coat.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.1, 1)
+    lib = coat.lib()
+    assert lib.coat_adamw_step(f, f, f, f, f, f, f, f, big, 128, 0, ctypes.byref(hp), None) == 3
+    assert L.coat_rmsnorm_fused(f, None, 2 ** 33 + 8, 1024, ctypes.c_float(1e-5), 128, f, f, None, None, None,
+                                None) == 3
