@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fp8_step_list_kernel(const StepL
 }
 
 template <int G, int VF, bool kBf16>
-hipError_t launch(const StepArgs &a, hipStream_t stream, int num_cus) {
+hipError_t launch(const StepArgs &a, hipStream_t stream, int /*num_cus*/) {
     constexpr auto kernel = &adamw_fp8_step_kernel<G, VF, kBf16>;
     const dim3 grid((unsigned)ceil_div(a.n_chunks, kBlock / 64));
     void *args[] = {const_cast<StepArgs *>(&a)};
