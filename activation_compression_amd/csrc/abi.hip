@@ -43,6 +43,25 @@ coat_status from_hip(hipError_t e) { return e == hipSuccess ? COAT_OK : COAT_ERR
 
 }  // namespace
 
+namespace coat {
+
+size_t stream_lds_bytes(size_t static_lds) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    int lds = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (lds <= 0) {
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            lds <= 0)
+            return 0;
+        if (dev < 64) cache[dev].store(lds, std::memory_order_relaxed);
+    }
+    const size_t per_block = (size_t)lds / kStreamBlocksPerCu;
+    return per_block > static_lds ? per_block - static_lds : 0;
+}
+
+}  // namespace coat
+
 extern "C" {
 
 const char *coat_status_string(coat_status s) {

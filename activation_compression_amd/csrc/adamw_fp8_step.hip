@@ -280,6 +280,8 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
 
 // The per-code dequantization table in LDS: [0, 256) m codes (E4M3), [256, 512)
 // v codes, both signs of a code byte mapping to its magnitude's entry.
+constexpr size_t kTabBytes = 512 * sizeof(float2);  // the kernels' static LDS
+
 __device__ __forceinline__ void fill_tab(float2 *tab, const StepParams &p) {
     const uint32_t t = threadIdx.x;
     tab[t] = p.log_tab[0][t & 127u];
@@ -335,7 +337,8 @@ hipError_t launch(const StepArgs &a, hipStream_t stream, int /*num_cus*/) {
     constexpr auto kernel = &adamw_fp8_step_kernel<G, VF, kBf16>;
     const dim3 grid((unsigned)ceil_div(a.n_chunks, kBlock / 64));
     void *args[] = {const_cast<StepArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args,
+                           stream_lds_bytes(kTabBytes), stream);
 }
 
 template <int G, int VF, bool kBf16>
@@ -343,7 +346,8 @@ hipError_t launch(const StepListArgs &a, hipStream_t stream, int) {
     constexpr auto kernel = &adamw_fp8_step_list_kernel<G, VF, kBf16>;
     const dim3 grid((unsigned)ceil_div(a.total_chunks, kBlock / 64));
     void *args[] = {const_cast<StepListArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kBlock), args,
+                           stream_lds_bytes(kTabBytes), stream);
 }
 
 template <int VF, bool kBf16, class Args>

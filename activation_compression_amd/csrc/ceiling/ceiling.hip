@@ -3,7 +3,7 @@
 //
 // step_skeleton moves exactly the bytes of the fused FP8-state AdamW step, with
 // the same launch shape (one 1024-parameter chunk per wave, 256-thread
-// workgroups, the same XCD-aware workgroup order) and the same per-lane layout (16 consecutive parameters: 64 B of
+// workgroups, the same XCD-aware workgroup order and residency cap) and the same per-lane layout (16 consecutive parameters: 64 B of
 // FP32 master weights, 32 B of BF16 gradient, 16 B of each FP8 moment, the
 // group's (amax, k) of both moments), but replaces the arithmetic with a
 // trivial dependence on every loaded byte.  copy_stream is a plain 16-byte-
@@ -67,15 +67,26 @@ __global__ __launch_bounds__(64) void copy_stream(const f4 *__restrict__ src, f4
 
 extern "C" {
 
-// n: parameters, a multiple of 1024 (group size 128).  Returns a hipError_t.
+// n: parameters, a multiple of 1024 (group size 128).  blocks_per_cu > 0 caps
+// the workgroups resident per CU (by reserving LDS), as the step does; 0
+// leaves residency to the hardware.  Returns a hipError_t.
 int coat_ceiling_step_skeleton(float *param, const uint16_t *grad, uint8_t *m_codes, float *m_amax, float *m_k,
-                               uint8_t *v_codes, float *v_amax, float *v_k, int64_t n, void *stream) {
+                               uint8_t *v_codes, float *v_amax, float *v_k, int64_t n, int blocks_per_cu,
+                               void *stream) {
     if (n <= 0 || n % 1024 != 0) return (int)hipErrorInvalidValue;
+    size_t lds = 0;
+    if (blocks_per_cu > 0) {
+        int dev = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+            per_cu > 0)
+            lds = (size_t)per_cu / (size_t)blocks_per_cu;
+    }
     SkelArgs a{param, reinterpret_cast<const uint32_t *>(grad), reinterpret_cast<uint32_t *>(m_codes),
                reinterpret_cast<uint32_t *>(v_codes), m_amax, m_k, v_amax, v_k, n / 1024};
     void *args[] = {&a};
     return (int)hipLaunchKernel(reinterpret_cast<const void *>(&step_skeleton), dim3((unsigned)((a.n_chunks + 3) / 4)),
-                                dim3(256), args, 0, (hipStream_t)stream);
+                                dim3(256), args, lds, (hipStream_t)stream);
 }
 
 // nbytes: a multiple of 16.

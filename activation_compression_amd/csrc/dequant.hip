@@ -75,7 +75,7 @@ template <typename K, typename... Args>
 hipError_t launch_k(K kernel, int64_t n_chunks, hipStream_t s, Args... args) {
     void *ptrs[] = {static_cast<void *>(&args)...};
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)ceil_div(n_chunks, kBlock / 64)),
-                           dim3(kBlock), ptrs, 0, s);
+                           dim3(kBlock), ptrs, stream_lds_bytes(0), s);
 }
 
 }  // namespace

@@ -60,6 +60,18 @@ struct StepListArgs {
 // FP8 format (0: E4M3, 1: E5M2), computed once per format in binary64.
 const float2 *fp8_log_table(int fmt);
 
+// Residency cap of the streaming kernels.  With fewer requests in flight
+// HBM serves this many-stream traffic better: measured on MI355X, the
+// optimizer step ran 20.66 ms at its register-limited 6 workgroups per CU,
+// 20.18 at 5 and 20.16 at 4, 20.5 at 3; SwiGLU 4% and the dequantization 2%
+// faster at 5 than at 8.  The casts and stage 1 ran up to 9% slower capped
+// and are left uncapped.  A kernel is held to
+// kStreamBlocksPerCu by requesting dynamic LDS it does not use:
+// stream_lds_bytes(static) bytes on top of its static LDS (abi.hip; 0 when the
+// device cannot be queried).
+constexpr int kStreamBlocksPerCu = 5;
+size_t stream_lds_bytes(size_t static_lds);
+
 // Every launcher takes the device's compute-unit count.  Streaming kernels
 // give each wave one 1024-element chunk (no grid-stride loop: the hardware
 // dispatcher then sweeps the arrays in order, which keeps DRAM pages open);

@@ -88,7 +88,7 @@ hipError_t launch_g(const uint16_t *gate, const uint16_t *up, int64_t n, uint16_
     const int64_t nc = ceil_div(n, kWaveElems);
     void *args[] = {&gate, &up, &n, const_cast<int64_t *>(&nc), &h, &hp, &gc, &gs, &uc, &us};
     return hipLaunchKernel(reinterpret_cast<const void *>(&swiglu_fused_kernel<G, kSave>),
-                           dim3((unsigned)ceil_div(nc, kBlock / 64)), dim3(kBlock), args, 0, s);
+                           dim3((unsigned)ceil_div(nc, kBlock / 64)), dim3(kBlock), args, stream_lds_bytes(0), s);
 }
 
 template <bool kSave>
