@@ -116,6 +116,26 @@ def memory_ceiling(theta, grad, st, n, alg_bytes, reps=3):
             "copy_gb_per_s": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1)}
 
 
+def state_diagnostics(st, sample=1 << 22):
+    """The expansion exponents of the optimizer state after the timed steps
+    (the COAT explainer gives k of 1-3 for m and 5-15 for v on real states):
+    percentiles of k over a fixed sample of groups, the share of groups with
+    k < 1 (wider than the format) and of all-zero groups."""
+    import torch
+
+    out = {}
+    ng = st["m_k"].numel()
+    idx = torch.linspace(0, ng - 1, min(sample, ng), device=st["m_k"].device).long()
+    for name in ("m", "v"):
+        k = st[f"{name}_k"][idx]
+        a = st[f"{name}_amax"][idx]
+        q = torch.quantile(k, torch.tensor([0.05, 0.5, 0.95], device=k.device)).tolist()
+        out[name] = {"k_p5_p50_p95": [round(x, 3) for x in q],
+                     "frac_k_below_1": round(float((k < 1).float().mean()), 5),
+                     "frac_zero_groups": round(float((a == 0).float().mean()), 5)}
+    return out
+
+
 def time_launches(fn, reps):
     """Average milliseconds of `fn` (launches on torch's current stream), HIP
     events on that stream around `reps` back-to-back calls after one warm-up."""
@@ -417,6 +437,7 @@ def main():
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * sum(step_ms[len(step_ms) // 2 - 1:][:2])
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
     traffic = measured_traffic()
+    diag = state_diagnostics(st)
     extra = None if args.no_extras else extras(coat, inputs, theta, grad, st, spec, G, step + 1)
     ceiling = memory_ceiling(theta, grad, st, n, alg["adamw_fp8_step"])
     if ceiling:
@@ -468,6 +489,7 @@ def main():
         "gpu_over_cpu_baseline": None if cpu is None else round(n / (ms_per_step * 1e-3) / cpu["value"], 1),
         "kernels": kernels,
         "extras": extra,
+        "state_diagnostics": diag,
         "step_hbm_gb_per_s": round(sum(alg.values()) / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
     }
