@@ -125,7 +125,11 @@ def state_diagnostics(st, sample=1 << 22):
 
     out = {}
     ng = st["m_k"].numel()
-    idx = torch.linspace(0, ng - 1, min(sample, ng), device=st["m_k"].device).long()
+    count = min(sample, ng)
+    # integer stride: every index below ng (a float32 linspace rounds its last
+    # index up to ng at this size)
+    idx = torch.arange(count, device=st["m_k"].device) * (ng // count)
+    assert int(idx[-1]) < ng
     for name in ("m", "v"):
         k = st[f"{name}_k"][idx]
         a = st[f"{name}_amax"][idx]
