@@ -25,32 +25,36 @@ __device__ __forceinline__ void load16(const uint16_t *p, uint32_t w[8]) {
 
 // Scaling constants for a (non-negative) absmax a: a = a_s 2^-sh, a_s in [1, 2).
 struct CastQ {
-    float mult;   // 448 * 2^sh: x * mult is exact
+    int sh;       // x 2^sh lies in [-2, 2] (exact: a power-of-two scale)
     float a_s;    // prescaled absmax
     float inv_s;  // RN(1 / a_s)
+    float m448;   // 448, or 0 for an all-zero tensor / slice (every code 0)
 };
 
 __device__ __forceinline__ CastQ cast_q(float a) {
     CastQ q;
-    if (!(a > 0.0f)) {  // all-zero tensor / slice: every code 0
-        q.mult = 0.0f; q.a_s = 1.0f; q.inv_s = 1.0f;
+    if (!(a > 0.0f)) {
+        q.sh = 0; q.a_s = 1.0f; q.inv_s = 1.0f; q.m448 = 0.0f;
         return q;
     }
     int e;
     const float ma = frexpf(a, &e);
     q.a_s = 2.0f * ma;
-    q.mult = __builtin_amdgcn_ldexpf(448.0f, 1 - e);
+    q.sh = 1 - e;
     q.inv_s = 1.0f / q.a_s;
+    q.m448 = 448.0f;
     return q;
 }
 
-// E4M3 codes of 16 BF16 values.
+// E4M3 codes of 16 BF16 values.  448 (x 2^sh) is exact -- a BF16 value in
+// [-2, 2] times 7 * 2^6 has at most 11 significant bits -- and neither factor
+// leaves the FP32 range for any finite BF16 slice, however large or small.
 __device__ __forceinline__ uint4 cast16(const uint32_t w[8], const CastQ &q) {
     float y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float x = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-        const float t = div_rn_from_rcp(x * q.mult, q.a_s, q.inv_s);
+        const float t = div_rn_from_rcp(__builtin_amdgcn_ldexpf(x, q.sh) * q.m448, q.a_s, q.inv_s);
         y[i] = __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
     }
     return make_uint4(cvt4<kE4M3>(y[0], y[1], y[2], y[3]), cvt4<kE4M3>(y[4], y[5], y[6], y[7]),

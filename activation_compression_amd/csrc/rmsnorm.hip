@@ -11,7 +11,10 @@
 // produced.
 //
 // One wave per row: the row (cols <= 8192) stays in registers between the
-// sum of squares and the normalization, so x is read from HBM once.  Lane l
+// sum of squares and the normalization, so x is read from HBM once.  The sum
+// of squares is taken in FP32 on the row scaled by a power of two (its max
+// |x| in [0.5, 1)), and mean + eps and its inverse square root in binary64,
+// so every finite BF16 row is in range.  Lane l
 // owns the 16-element pieces l, l + 64, l + 128, ... of its row; a 1xG slice
 // is G/16 adjacent lanes of one of those 64-piece sweeps.
 #include "cast.hpp"
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fused_kernel(const uint16_t *_
     const int pieces = cols >> 4;
     const int64_t base = row * (int64_t)cols;
     uint32_t xw[PPL][8];
-    float ss = 0.0f;
+    uint32_t am = 0u;
 #pragma unroll
     for (int c = 0; c < PPL; ++c) {
         const int p = c * 64 + lane;
@@ -52,15 +55,27 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fused_kernel(const uint16_t *_
 #pragma unroll
             for (int i = 0; i < 8; ++i) xw[c][i] = 0u;
         }
+        am = max(am, absmax16(xw[c]));
+    }
+    // The squares are summed after an exact power-of-two scale that brings the
+    // row's max |x| into [0.5, 1), so no finite BF16 row over- or underflows
+    // FP32; the per-row remainder runs in binary64.
+    const float amf = __uint_as_float(run_max<64>(am) << 16);
+    const int e = amf > 0.0f ? __builtin_amdgcn_frexp_expf(amf) : 0;
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < PPL; ++c) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float a = bf16_lo(xw[c][i]), b = bf16_hi(xw[c][i]);
+            const float a = __builtin_amdgcn_ldexpf(bf16_lo(xw[c][i]), -e);
+            const float b = __builtin_amdgcn_ldexpf(bf16_hi(xw[c][i]), -e);
             ss = __builtin_fmaf(a, a, ss);
             ss = __builtin_fmaf(b, b, ss);
         }
     }
     ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)cols + eps);  // correctly rounded divide and sqrt
+    const double mean = ldexp((double)ss / (double)cols, 2 * e);
+    const float r = (float)(1.0 / sqrt(mean + (double)eps));
     if (rstd && lane == 0) rstd[row] = r;
     const int64_t gbase = row * (int64_t)(cols / G);
 #pragma unroll

@@ -363,10 +363,17 @@ def check_rmsnorm(x, w, G, eps, y, yp, rstd, saved, what, threads=1):
                                            (9, 3072, 512)])
 @pytest.mark.parametrize("weighted, save", [(False, False), (True, True)])
 def test_rmsnorm_fused_small(rows, cols, G, weighted, save):
-    """(5, 2080) ends in a partial 64-piece sweep; (7, 8192) is the widest row."""
+    """(5, 2080) ends in a partial 64-piece sweep; (7, 8192) is the widest row.
+    Row 3 holds values near 1e30 (their squares overflow FP32), row 4 values
+    near 1e-37 (their squares underflow it)."""
     x = act(rows, cols, seed=rows * 7 + G)
     x[1] = 0                  # zero row: y = 0, rstd = 1/sqrt(eps)
     x[2, :G] = 0x8000         # a -0 slice
+    g = torch.Generator().manual_seed(rows + cols)
+    big = torch.randn(cols, generator=g) * 1e30     # squares beyond FP32
+    tiny = torch.randn(cols, generator=g) * 1e-37   # squares below FP32, BF16 subnormals among them
+    x[3] = big.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    x[4] = tiny.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     w = inputs.gen_norm_weight(cols, seed=cols).numpy().view(np.uint16) if weighted else None
     flush(f"rmsnorm {rows}x{cols} G={G} weighted={weighted} save={save}")
     y, yp, rstd, saved = gpu_rmsnorm(x, w, G, 1e-5, save)
@@ -396,3 +403,49 @@ def test_rmsnorm_fused_full_size():
     y, yp, rstd, saved = gpu_rmsnorm(x, w, 128, 1e-5, True)
     frac = check_rmsnorm(x, w, 128, 1e-5, y, yp, rstd, saved, spec.name, threads=THREADS)
     flush(f"y identical fraction {frac:.7f}")
+
+
+def _bf16_of(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_group_cast_at_the_ends_of_the_bf16_range(G):
+    """Slices whose max |x| is near the top of BF16 (3e38), near 1e30, near
+    1e-37 and among the BF16 subnormals (down to 2^-133): the cast's scaled
+    numerator 448 x / a must neither overflow nor flush, bit for bit with the
+    oracle."""
+    rows, cols = 6, 1024
+    g = torch.Generator().manual_seed(G)
+    x = np.empty((rows, cols), np.uint16)
+    x[0] = _bf16_of(torch.randn(cols, generator=g) * 1e37)   # finite: |N(0,1)| < 34 here
+    x[1] = _bf16_of(torch.randn(cols, generator=g) * 1e30)
+    x[2] = _bf16_of(torch.randn(cols, generator=g) * 1e-37)
+    x[3] = _bf16_of(torch.randn(cols, generator=g) * 1e-39)   # BF16 subnormals
+    x[4] = np.random.default_rng(G).integers(1, 0x80, cols).astype(np.uint16) | \
+        np.where(np.arange(cols) % 2, 0x8000, 0).astype(np.uint16)  # the smallest subnormals, both signs
+    x[5] = _bf16_of(torch.randn(cols, generator=g))
+    x[5, :G] = np.where(np.arange(G) % 3 == 0, 0x7F7F, 0x0001)  # max and min magnitude in one slice
+    assert np.isfinite((x.astype(np.uint32) << 16).view(np.float32)).all()  # infinities are outside the contract
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(x.size // G, device="cuda")
+    partial = torch.empty(x.size // G, device="cuda")
+    coat.coat_quant_group(dev(x), codes, scales, partial, group_size=G)
+    torch.cuda.synchronize()
+    rc, rs, rp = orc.quant_group(x, G)
+    assert (host(scales) == rs).all() and (host(partial) == rp).all()
+    assert (norm0(host(codes)) == rc).all()
+
+
+@pytest.mark.parametrize("scale", [1e37, 1e30, 1e-37, 1e-39])
+def test_per_tensor_cast_at_the_ends_of_the_bf16_range(scale):
+    g = torch.Generator().manual_seed(3)
+    x = _bf16_of(torch.randn(4096, generator=g) * scale)
+    assert np.isfinite((x.astype(np.uint32) << 16).view(np.float32)).all()
+    A = np.float32(np.abs((x.astype(np.uint32) << 16).view(np.float32)).max())
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, device="cuda")
+    coat.coat_quant_per_tensor(dev(x), torch.tensor([A], device="cuda"), codes, sc)
+    torch.cuda.synchronize()
+    rc, rs = orc.quant_per_tensor(x, A)
+    assert host(sc)[0] == rs and (norm0(host(codes)) == rc).all()
