@@ -65,18 +65,16 @@ const float2 *fp8_log_table(int fmt);
 // optimizer step ran 20.66 ms at its register-limited 6 workgroups per CU,
 // 20.18 at 5 and 20.16 at 4, 20.5 at 3; SwiGLU 4% and the dequantization 2%
 // faster at 5 than at 8.  The casts and stage 1 ran up to 9% slower capped
-// and are left uncapped.  A kernel is held to
-// kStreamBlocksPerCu by requesting dynamic LDS it does not use:
-// stream_lds_bytes(static) bytes on top of its static LDS (abi.hip; 0 when the
-// device cannot be queried).
+// and are left uncapped.  A kernel is held to kStreamBlocksPerCu by
+// requesting dynamic LDS it does not use: stream_lds_bytes(static) bytes on
+// top of its static LDS (abi.hip; 0 when the device cannot be queried).
 constexpr int kStreamBlocksPerCu = 5;
 size_t stream_lds_bytes(size_t static_lds);
 
-// Every launcher takes the device's compute-unit count.  Streaming kernels
-// give each wave one 1024-element chunk (no grid-stride loop: the hardware
-// dispatcher then sweeps the arrays in order, which keeps DRAM pages open);
-// the small reduction kernels are grid-stride with as many workgroups as can
-// be resident at once.
+// Streaming kernels give each wave one 1024-element chunk (no grid-stride
+// loop: the hardware dispatcher then sweeps the arrays in order, which keeps
+// DRAM pages open); the small reduction kernel of stage 2 is grid-stride and
+// sizes its grid from the device's compute-unit count (num_cus).
 hipError_t launch_adamw_fp8_step(const StepArgs &a, int group_size, int v_format,
                                  hipStream_t stream, int num_cus);
 hipError_t launch_adamw_fp8_step_list(const StepListArgs &a, int group_size, int v_format, hipStream_t stream);
