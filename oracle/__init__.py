@@ -18,7 +18,9 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# COAT_ORACLE_LIB names another build of coat_oracle.c (the pin tests' own
+# check that planted mistakes fail them loads mutated builds this way).
+LIB_PATH = os.environ.get("COAT_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 E4M3, E5M2, E2M2 = 0, 1, 2
 FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m2": E2M2}

@@ -12,12 +12,12 @@ SRC = os.path.join(HERE, "coat_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
+FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off", "-fno-strict-aliasing",
+         "-Wall", "-Wextra"]
+
+
 def build(verbose: bool = False) -> str:
-    cmd = [
-        "gcc", "-std=c11", "-O2", "-fPIC", "-shared",
-        "-fno-fast-math", "-ffp-contract=off", "-fno-strict-aliasing",
-        "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm",
-    ]
+    cmd = ["gcc", *FLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
