@@ -222,10 +222,16 @@ def bf16_step(x):
 FLUSH_GATE = -87.0
 
 
+def identical_enough(n_same, n, what):
+    """At least 99.99% identical (at least one difference allowed)."""
+    bad = n - n_same
+    assert bad <= max(1, int(1e-4 * n)), f"{what}: {bad} of {n} not identical"
+
+
 def assert_h_close(h_gpu, h_ref, gate, up, what):
     """h in value space within one BF16 step of the oracle's (the kernel's FP32
     silu is a few FP32 ulps off, which moves a BF16 rounding by one step at
-    most), at least 99.9% identical; flushed tails as documented above."""
+    most), at least 99.99% identical; flushed tails as documented above."""
     hg, hr = bf16_f32(h_gpu), bf16_f32(h_ref)
     g, u = bf16_f32(gate).reshape(-1), bf16_f32(up).reshape(-1)
     flushed = (g < FLUSH_GATE) & (hg == 0)
@@ -235,7 +241,7 @@ def assert_h_close(h_gpu, h_ref, gate, up, what):
     same = (h_gpu == h_ref) | flushed
     parity.BF16_STATS.append((what, same.size, int(same.size - np.count_nonzero(same))))
     frac = np.count_nonzero(same) / same.size
-    assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
+    identical_enough(np.count_nonzero(same), same.size, what)
     return frac
 
 
@@ -350,7 +356,7 @@ def check_rmsnorm(x, w, G, eps, y, yp, rstd, saved, what, threads=1):
     assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond one BF16 step"
     frac = np.count_nonzero(y == y_ref) / y.size
     parity.BF16_STATS.append((f"rmsnorm {what}", y.size, int(y.size - np.count_nonzero(y == y_ref))))
-    assert frac >= 0.999, f"{what}: only {frac:.6f} identical"
+    identical_enough(np.count_nonzero(y == y_ref), y.size, what)
     assert (yp == np.abs(yg).reshape(-1, G).max(axis=1)).all(), what
     assert (np.abs(yp - p_ref) <= bf16_step(p_ref)).all(), what
     if saved is not None:
