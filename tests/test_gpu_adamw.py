@@ -8,7 +8,7 @@ import torch
 
 import oracle as orc
 from activation_compression_amd import coat, inputs
-from parity import (LR, assert_codes, assert_step_parity, assert_theta, dev, flush, gpu_hp, gpu_step, orc_hp,
+from parity import (LR, assert_step_parity, assert_theta, dev, flush, gpu_hp, gpu_step, orc_hp,
                     host, np_state, oracle_step)
 
 pytestmark = [pytest.mark.gpu,

@@ -7,7 +7,6 @@ and the optimizer step (arena and tensor-list forms) can be captured once
 and replayed; each replay must reproduce the eager result bit for bit.  Each
 test replays several times with new inputs written eagerly in between and
 the outputs clobbered before the eager reference run."""
-import numpy as np
 import pytest
 import torch
 
