@@ -200,6 +200,20 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     out[f"adamw_fp8_step_list_{len(views)}_tensors"] = entry(n * (14.0 + 32.0 / G), ms, n)
     del tl, views
 
+    # the stress set (64 Mi params, gradients over ten decades, 5% zeros) for
+    # G in {32, 128, 512} and both v formats, and the single 1024 x 1024 tensor
+    # (a launch-bound correctness workload): average of 10 steps after 2
+    for sp in [inputs.stress(g_, f_) for g_ in (32, 128, 512) for f_ in ("e4m3", "e5m2")] + [inputs.single_1024()]:
+        ns = sp.numel
+        ths = inputs.gen_params(sp, device="cuda")
+        gs_ = inputs.gen_grads(sp, 1, device="cuda")
+        sts = inputs.fresh_state(ns, sp.group_size, device="cuda")
+        ms_s = time_launches(lambda i: coat.coat_adamw_step(
+            ths, gs_, sts["m_codes"], sts["m_amax"], sts["m_k"], sts["v_codes"], sts["v_amax"], sts["v_k"],
+            group_size=sp.group_size, v_format=sp.v_fmt, hp=hp(i + 1)), 10)
+        out[f"adamw_fp8_step_{sp.name}"] = entry(ns * (14.0 + 32.0 / sp.group_size), ms_s, ns)
+        del ths, gs_, sts
+
     # the OLMo-1B-shaped parameter set (v in E5M2): five steps from a fresh
     # state, the median of steps 2-5 (each step timed alone)
     s1 = inputs.olmo_1b()
