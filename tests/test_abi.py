@@ -248,3 +248,20 @@ def test_sizes_beyond_the_launch_grid_are_rejected(L):
     assert lib.coat_adamw_step(f, f, f, f, f, f, f, f, big, 128, 0, ctypes.byref(hp), None) == 3
     assert L.coat_rmsnorm_fused(f, None, 2 ** 33 + 8, 1024, ctypes.c_float(1e-5), 128, f, f, None, None, None,
                                 None) == 3
+
+
+def test_empty_inputs_are_rejected(L):
+    """Zero-size inputs are a shape error everywhere (nothing is enqueued)."""
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    from activation_compression_amd import coat
+    lib = coat.lib()
+    hp = coat.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.1, 1)
+    assert lib.coat_adamw_step(f, f, f, f, f, f, f, f, 0, 128, 0, ctypes.byref(hp), None) == 3
+    assert L.coat_quant_per_tensor(f, 0, f, f, f, None) == 3
+    assert L.coat_dequant_per_tensor(f, 0, f, f, None) == 3
+    assert L.coat_quant_group(f, 0, 4096, 128, f, f, None, None) == 3
+    assert L.coat_quant_group(f, 16, 0, 128, f, f, None, None) == 3
+    assert L.coat_dequant_group(f, 16, 0, 128, f, f, None) == 3
+    assert L.coat_swiglu_fused(f, f, 0, 256, 128, f, f, None, None, None, None, None) == 3
+    assert L.coat_group_absmax(f, 16, 0, 128, f, f, None) == 3
