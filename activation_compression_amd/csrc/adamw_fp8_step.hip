@@ -22,10 +22,23 @@
 // range can produce, so zero needs no branch.
 //
 // Requantization  c = RNE_sat(sign(x) MAX (|x| / amax)^k)  forms the ratio
-// |x| / amax correctly rounded (power-of-two prescale, RN reciprocal and one
-// Markstein correction), then exp2(k log2 r) with the native transcendental
-// instructions, and converts with v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32.  The
-// group maximum gives r = 1 exactly and lands on MAX exactly.
+// |x| / amax correctly rounded (RN reciprocal and one Markstein correction),
+// then exp2(k log2 r) with the native transcendental instructions, and
+// converts with v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32.  The group maximum gives
+// r = 1 exactly and lands on MAX exactly.
+//
+// Wide groups.  FP32 spans 2^277 from the smallest denormal to the largest
+// value, so a group's max / min can exceed what the ratio |x| / amax (and the
+// factor 2^(L/k) of dequantization) can hold: |x| / amax below 2^-126 loses
+// bits or flushes to zero, and the native log2 flushes denormal inputs.  A
+// group whose range passes 2^120 (k < log2 R_fmt / 120), or whose amax lies
+// outside [2^-120, 2^120], takes the log domain instead: |x| = mx 2^ex and
+// amax = ma 2^ea split exactly (frexp), log2(|x| / amax) = (ex - ea) +
+// log2(mx / ma) with the mantissa quotient correctly rounded in (1/2, 2); and
+// dequantization splits 2^(L/k) = 2^f 2^n (n = rint(L/k), exact) and applies
+// 2^(n + ea) last with ldexp.  Such groups are rare (gradients spanning
+// dozens of decades within G values), so the branch is taken by whole lanes
+// and costs the common path a compare.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -69,31 +82,49 @@ __device__ __forceinline__ float dequant(uint32_t byte, const float2 *tab, float
     return mag;
 }
 
+// The same inverse expansion for a wide group (amax = ma 2^ea, ma_ln2 = ma
+// ln2): 2^(L/k) = 2^f 2^n with n = rint(ph) and f = ph - n exact, the power
+// 2^(n + ea) applied last.  A zero code's ph is below -2^90; n is clamped at
+// -1024 so the exponent stays an int, and 2^f with f = ph + 1024 is then 0.
+template <bool kSigned>
+__device__ __forceinline__ float dequant_wide(uint32_t byte, const float2 *tab, float ma, float ma_ln2, int ea,
+                                              float ih, float il) {
+    const float2 L = tab[byte];
+    const float ph = L.x * ih;
+    float pl = __builtin_fmaf(L.x, ih, -ph);
+    pl = __builtin_fmaf(L.x, il, pl);
+    pl = __builtin_fmaf(L.y, ih, pl);
+    const float n = __builtin_fmaxf(__builtin_rintf(ph), -1024.0f);
+    const float mag = __builtin_amdgcn_ldexpf(
+        __builtin_amdgcn_exp2f(ph - n) * __builtin_fmaf(ma_ln2, pl, ma), ea + (int)n);
+    if constexpr (kSigned)
+        return __uint_as_float(__float_as_uint(mag) | ((byte & 0x80u) << 24));
+    return mag;
+}
+
+// A stored group the fast dequantization cannot reproduce: 2^(L/k) for the
+// smallest nonzero code, 2^(-log2 R_fmt / k), would pass 2^-120.
+__device__ __forceinline__ bool wide_k(float k, float log2_range) { return k * 120.0f < log2_range; }
+
 // Per-group quantization parameters of one new moment.
 struct GroupQ {
     float amax;   // stored scale: the group's max |x|
     float k;      // stored expansion exponent
-    float amq;    // amax, or amax 2^sh in [1, 2) for groups outside [2^-120, 2^120]
+    float amq;    // amax; for a wide group its mantissa ma in [1/2, 1)
     float invq;   // RN(1 / amq)
-    int sh;       // prescale exponent (0 on the common path)
+    int ea;       // wide group: amax = ma 2^ea
+    int wide;     // nonzero: the log-domain requantization
 };
 
 // mx: bits of max |x|; mn: bits of min nonzero |x| (0 when none).
 __device__ __forceinline__ GroupQ group_q(uint32_t mx, uint32_t mn, float log2_range) {
     GroupQ q;
     q.amax = __uint_as_float(mx);
-    q.k = 1.0f; q.amq = 1.0f; q.invq = 1.0f; q.sh = 0;
+    q.k = 1.0f; q.amq = 1.0f; q.invq = 1.0f; q.ea = 0; q.wide = 0;
     if (mx == 0u) return q;  // all-zero group: every code is 0
-    int ea;
     const float ma = __builtin_amdgcn_frexp_mantf(q.amax);  // [0.5, 1)
-    ea = __builtin_amdgcn_frexp_expf(q.amax);
-    if (mx < 0x03800000u || mx > 0x7B800000u) {  // outside [2^-120, 2^120]
-        q.sh = 1 - ea;
-        q.amq = 2.0f * ma;
-    } else {
-        q.amq = q.amax;
-    }
-    q.invq = rcp_rn(q.amq);
+    const int ea = __builtin_amdgcn_frexp_expf(q.amax);
+    bool wide = mx < 0x03800000u || mx > 0x7B800000u;  // outside [2^-120, 2^120]
     if (mn != mx) {
         const float mb = __builtin_amdgcn_frexp_mantf(__uint_as_float(mn));
         const int eb = __builtin_amdgcn_frexp_expf(__uint_as_float(mn));
@@ -102,7 +133,12 @@ __device__ __forceinline__ GroupQ group_q(uint32_t mx, uint32_t mn, float log2_r
         const float lg = (float)(ea - eb) + __builtin_amdgcn_logf(ratio);
         // k = log2(R_fmt) / log2(amax / amin): (amax/amin)^k spans MAX / min_subnormal
         q.k = div_rn_from_rcp(log2_range, lg, rcp_rn(lg));
+        wide = wide || lg > 120.0f;
     }
+    q.amq = wide ? ma : q.amax;
+    q.invq = rcp_rn(q.amq);
+    q.ea = ea;
+    q.wide = wide;
     return q;
 }
 
@@ -128,6 +164,20 @@ template <int F>
 __device__ __forceinline__ float expand(float xs, float amq, float invq, float k) {
     const float r = div_rn_from_rcp(xs, amq, invq);  // RN(|x| / amax) <= 1
     const float y = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_amdgcn_logf(r), k, Log2Max<F>::v));
+    return __builtin_fminf(y, Fp8<F>::kMax);
+}
+
+// The same for a wide group (amax = ma 2^ea, inv_ma = RN(1 / ma)): the
+// exponent difference enters through the FMA exactly, the mantissa quotient
+// lies in (1/2, 2), and no intermediate leaves the normal range.  |x| = 0
+// gives log2(0) = -inf and code 0.
+template <int F>
+__device__ __forceinline__ float expand_wide(float ax, float ma, float inv_ma, int ea, float k) {
+    const float mx = __builtin_amdgcn_frexp_mantf(ax);
+    const int ex = __builtin_amdgcn_frexp_expf(ax);
+    const float q = div_rn_from_rcp(mx, ma, inv_ma);
+    const float t = __builtin_fmaf(__builtin_amdgcn_logf(q), k, Log2Max<F>::v);
+    const float y = __builtin_amdgcn_exp2f(__builtin_fmaf((float)(ex - ea), k, t));
     return __builtin_fminf(y, Fp8<F>::kMax);
 }
 
@@ -182,22 +232,39 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
     float ihm, ilm, ihv, ilv;
     recip2(k_m, ihm, ilm);
     recip2(k_v, ihv, ilv);
-    const float am_m_ln2 = am_m * kLn2, am_v_ln2 = am_v * kLn2;
 
-    // dequantize, AdamW in FP32, group statistics of the new moments
+    // dequantize the old moments into m1 / v1 (a lane's groups decide its path)
     float m1[16], v1[16];
+    if (!(wide_k(k_m, p.m_log2_range) || wide_k(k_v, p.v_log2_range))) {
+        const float am_m_ln2 = am_m * kLn2, am_v_ln2 = am_v * kLn2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            m1[i] = dequant<true>((mw[i >> 2] >> (8 * (i & 3))) & 0xFFu, tab, am_m, am_m_ln2, ihm, ilm);
+            v1[i] = dequant<false>((vw[i >> 2] >> (8 * (i & 3))) & 0xFFu, tab + 256, am_v, am_v_ln2, ihv, ilv);
+        }
+    } else {
+        const float ma_m = __builtin_amdgcn_frexp_mantf(am_m), ma_v = __builtin_amdgcn_frexp_mantf(am_v);
+        const int ea_m = __builtin_amdgcn_frexp_expf(am_m), ea_v = __builtin_amdgcn_frexp_expf(am_v);
+        const float ma_m_ln2 = ma_m * kLn2, ma_v_ln2 = ma_v * kLn2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            m1[i] = dequant_wide<true>((mw[i >> 2] >> (8 * (i & 3))) & 0xFFu, tab, ma_m, ma_m_ln2, ea_m, ihm, ilm);
+            v1[i] = dequant_wide<false>((vw[i >> 2] >> (8 * (i & 3))) & 0xFFu, tab + 256, ma_v, ma_v_ln2, ea_v,
+                                        ihv, ilv);
+        }
+    }
+
+    // AdamW in FP32, group statistics of the new moments
     float mx_m = 0.0f, mx_v = 0.0f;
     uint32_t mn_m = ~0u, mn_v = ~0u;  // min over the bits of 2|x| - 2: zero wraps to the top
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t cm = (mw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const uint32_t cv = (vw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const float m0 = dequant<true>(cm, tab, am_m, am_m_ln2, ihm, ilm);
-        const float v0 = dequant<false>(cv, tab + 256, am_v, am_v_ln2, ihv, ilv);
+        const float m0 = m1[i], v0 = v1[i];
         const float g = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
 
         const float m = __builtin_fmaf(p.beta1, m0, p.omb1 * g);
-        const float v = __builtin_fmaf(p.beta2, v0, p.omb2 * (g * g));
+        // (1 - b2) g first: g^2 alone leaves FP32 for |g| > 1.8e19, (1 - b2) g^2 only when v must
+        const float v = __builtin_fmaf(p.beta2, v0, (p.omb2 * g) * g);
         const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(v), p.inv_sqrt_bc2, p.eps);
         const float u = m * __builtin_amdgcn_rcpf(den);
         th[i] = __builtin_fmaf(th[i], p.decay, -p.step_size * u);
@@ -240,11 +307,11 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
     const float kq_m = run_bcast<LPG, 0>(q.k);
     const float amq_v = run_bcast<LPG, 1>(q.amq), inv_v = run_bcast<LPG, 1>(q.invq);
     const float kq_v = run_bcast<LPG, 1>(q.k);
-    const int sh_m = __float_as_int(run_bcast<LPG, 0>(__int_as_float(q.sh)));
-    const int sh_v = __float_as_int(run_bcast<LPG, 1>(__int_as_float(q.sh)));
+    const int wide_m = __float_as_int(run_bcast<LPG, 0>(__int_as_float(q.wide)));
+    const int wide_v = __float_as_int(run_bcast<LPG, 1>(__int_as_float(q.wide)));
 
     uint32_t om[4], ov[4];
-    if ((sh_m | sh_v) == 0) {
+    if ((wide_m | wide_v) == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float ym[4], yv[4];
@@ -257,16 +324,20 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
             om[t] = cvt4<kE4M3>(ym[0], ym[1], ym[2], ym[3]);
             ov[t] = cvt4<VF>(yv[0], yv[1], yv[2], yv[3]);
         }
-    } else {  // a group max outside [2^-120, 2^120]: power-of-two prescale first
+    } else {  // a wide group in this lane: the log-domain form for both moments
+        const int ea_m = __float_as_int(run_bcast<LPG, 0>(__int_as_float(q.ea)));
+        const int ea_v = __float_as_int(run_bcast<LPG, 1>(__int_as_float(q.ea)));
+        const float ma_m = wide_m ? amq_m : __builtin_amdgcn_frexp_mantf(amq_m);
+        const float ma_v = wide_v ? amq_v : __builtin_amdgcn_frexp_mantf(amq_v);
+        const float ia_m = wide_m ? inv_m : rcp_rn(ma_m), ia_v = wide_v ? inv_v : rcp_rn(ma_v);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float ym[4], yv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float xm = m1[4 * t + u];
-                ym[u] = with_sign_of(expand<kE4M3>(__builtin_amdgcn_ldexpf(__builtin_fabsf(xm), sh_m),
-                                                   amq_m, inv_m, kq_m), xm);
-                yv[u] = expand<VF>(__builtin_amdgcn_ldexpf(v1[4 * t + u], sh_v), amq_v, inv_v, kq_v);
+                ym[u] = with_sign_of(expand_wide<kE4M3>(__builtin_fabsf(xm), ma_m, ia_m, ea_m, kq_m), xm);
+                yv[u] = expand_wide<VF>(v1[4 * t + u], ma_v, ia_v, ea_v, kq_v);
             }
             om[t] = cvt4<kE4M3>(ym[0], ym[1], ym[2], ym[3]);
             ov[t] = cvt4<VF>(yv[0], yv[1], yv[2], yv[3]);

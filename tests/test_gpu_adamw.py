@@ -491,3 +491,26 @@ def test_checkpoint_resume_bit_identical(v_fmt):
     assert (host(th_c).view(np.uint32) == host(th_a).view(np.uint32)).all()
     for k in st_a:
         assert (host(st_c[k]).view(np.uint8) == host(st_a[k]).view(np.uint8)).all(), k
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_gradients_at_the_ends_of_the_range(v_fmt):
+    """|g| log-uniform over 10^-30 .. 10^20.5 (random signs): (1 - b2) g^2 must
+    be formed without overflowing FP32 for every g whose second moment fits
+    FP32, and vanishing squares must behave as the oracle's; two lockstep
+    steps, G = 128."""
+    rng = np.random.default_rng(11)
+    n, G = 128 * 1024, 128
+    spec = inputs.ArenaSpec("wide-grads", 6, (("w", (n // 128, 128)),), v_fmt, G, "tensor")
+    theta = inputs.gen_params(spec).numpy()
+    st = np_state(n, G)
+    for t in (1, 2):
+        mag = 10.0 ** rng.uniform(-30.0, 20.5, n)
+        g32 = (mag * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+        g = torch.from_numpy(g32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        flush(f"wide gradients step {t} v={v_fmt}")
+        gpu = gpu_step(theta, g, st, G, v_fmt, t)
+        ref = oracle_step(theta, g, st, G, v_fmt, t)
+        assert np.isfinite(gpu[0]).all() and np.isfinite(gpu[1]["v_amax"]).all()
+        assert_step_parity(gpu, ref, v_fmt, f"wide gradients step {t}", prev=None if t == 1 else st)
+        theta, st = ref
