@@ -117,26 +117,39 @@ struct GroupQ {
 };
 
 // mx: bits of max |x|; mn: bits of min nonzero |x| (0 when none).
+//
+// k = log2(R_fmt) / log2(amax / amin) takes its denominator from the very
+// expression requantization evaluates for amin (-log2 of RN(amin / amax), or
+// its exponent-split form in a wide group), so that amin lands on the
+// smallest subnormal whatever the ratio's rounding.  A group only a few ulps
+// wide would otherwise meet two roundings of one ratio that differ by tens of
+// percent -- enough to push its smallest element below half the smallest
+// subnormal, to code 0.
 __device__ __forceinline__ GroupQ group_q(uint32_t mx, uint32_t mn, float log2_range) {
     GroupQ q;
     q.amax = __uint_as_float(mx);
     q.k = 1.0f; q.amq = 1.0f; q.invq = 1.0f; q.ea = 0; q.wide = 0;
     if (mx == 0u) return q;  // all-zero group: every code is 0
+    const float amin = __uint_as_float(mn);
     const float ma = __builtin_amdgcn_frexp_mantf(q.amax);  // [0.5, 1)
     const int ea = __builtin_amdgcn_frexp_expf(q.amax);
-    bool wide = mx < 0x03800000u || mx > 0x7B800000u;  // outside [2^-120, 2^120]
+    const float mb = __builtin_amdgcn_frexp_mantf(amin);
+    const int eb = __builtin_amdgcn_frexp_expf(amin);
+    const float inv_ma = rcp_rn(ma);
+    // log2(amin / amax) as expand_wide evaluates it for amin
+    const float lw = (float)(eb - ea) + __builtin_amdgcn_logf(div_rn_from_rcp(mb, ma, inv_ma));
+    const bool wide = mx < 0x03800000u || mx > 0x7B800000u || lw < -120.0f;  // amax outside [2^-120, 2^120]
+    q.amq = wide ? ma : q.amax;
+    q.invq = wide ? inv_ma : rcp_rn(q.amax);
     if (mn != mx) {
-        const float mb = __builtin_amdgcn_frexp_mantf(__uint_as_float(mn));
-        const int eb = __builtin_amdgcn_frexp_expf(__uint_as_float(mn));
-        // log2(amax / amin) = (ea - eb) + log2(ma / mb), the quotient correctly rounded
-        const float ratio = div_rn_from_rcp(ma, mb, rcp_rn(mb));
-        const float lg = (float)(ea - eb) + __builtin_amdgcn_logf(ratio);
+        // log2(amax / amin) as expand evaluates -log2(amin / amax)
+        float lg = -(wide ? lw : __builtin_amdgcn_logf(div_rn_from_rcp(amin, q.amq, q.invq)));
+        // Two distinct floats differ by at least 2^-24 relative: the true value is at least
+        // log2(1 + 2^-24) ~ 8.6e-8, and the clamp keeps k finite and positive whatever the log returns.
+        lg = __builtin_fmaxf(lg, 8.5e-8f);
         // k = log2(R_fmt) / log2(amax / amin): (amax/amin)^k spans MAX / min_subnormal
         q.k = div_rn_from_rcp(log2_range, lg, rcp_rn(lg));
-        wide = wide || lg > 120.0f;
     }
-    q.amq = wide ? ma : q.amax;
-    q.invq = rcp_rn(q.amq);
     q.ea = ea;
     q.wide = wide;
     return q;

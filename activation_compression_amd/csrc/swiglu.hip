@@ -15,7 +15,8 @@
 // native exp2 and reciprocal), stored as BF16 (round to nearest even); the
 // slice maxima are taken over |h| as stored.  Each lane owns 16 consecutive
 // elements; a 1xG slice is G/16 adjacent lanes; one 1024-element chunk per
-// wave.
+// wave.  Gates below -80 take a second, exponent-split form (see swiglu_far),
+// run only by lanes that hold one.
 #include "cast.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -25,9 +26,32 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-__device__ __forceinline__ float silu(float x) {
-    const float e = __builtin_amdgcn_exp2f(-x * kLog2e);
-    return x * __builtin_amdgcn_rcpf(1.0f + e);
+// Gates below this take swiglu_far: there e^-g > 2^115 nears the top of FP32
+// and silu(g) itself reaches FP32's denormals from g < -87.3, while the
+// product with u can still be a normal number.
+constexpr float kFarGate = -80.0f;
+
+// silu(g) u for g >= kFarGate.
+__device__ __forceinline__ float swiglu_near(float g, float u) {
+    return (g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e))) * u;
+}
+
+// silu(g) u for g < kFarGate.  silu(g) = g e^g / (1 + e^g) is g e^g to within
+// e^g < 2^-115 relative, and |g e^g u| = (mg mu 2^f) 2^(eg + eu + n) with
+// |g| = mg 2^eg and |u| = mu 2^eu split exactly (frexp) and g log2 e = n + f
+// (n = rint, f exact): every factor stays normal and the power of two is
+// applied last, so h is rounded at its own magnitude.  The sign is that of
+// -u (g < 0).  A gate so negative that g log2 e overflows gives n = -1024
+// (clamped, to keep the exponent an int), f = -inf and h = 0.
+__device__ __forceinline__ float swiglu_far(float g, float u) {
+    const float t = g * kLog2e;
+    const float n = __builtin_fmaxf(__builtin_rintf(t), -1024.0f);
+    const float ag = __builtin_fabsf(g), au = __builtin_fabsf(u);
+    const float m = (__builtin_amdgcn_frexp_mantf(ag) * __builtin_amdgcn_frexp_mantf(au)) *
+                    __builtin_amdgcn_exp2f(t - n);
+    const float mag = __builtin_amdgcn_ldexpf(
+        m, __builtin_amdgcn_frexp_expf(ag) + __builtin_amdgcn_frexp_expf(au) + (int)n);
+    return with_sign_of(mag, -u);
 }
 
 template <int G, bool kSaveInputs>
@@ -51,11 +75,21 @@ __global__ __launch_bounds__(kBlock) void swiglu_fused_kernel(const uint16_t *__
         load16(up + e0, uw);
     }
     uint32_t hw[8];
+    bool far = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float h0 = silu(bf16_lo(gw[i])) * bf16_lo(uw[i]);
-        const float h1 = silu(bf16_hi(gw[i])) * bf16_hi(uw[i]);
-        hw[i] = bf16x2(h0, h1);
+        const float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
+        far |= (g0 < kFarGate) | (g1 < kFarGate);
+        hw[i] = bf16x2(swiglu_near(g0, bf16_lo(uw[i])), swiglu_near(g1, bf16_hi(uw[i])));
+    }
+    if (far) {  // a gate below kFarGate in this lane's 16 elements
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
+            const float u0 = bf16_lo(uw[i]), u1 = bf16_hi(uw[i]);
+            hw[i] = bf16x2(g0 < kFarGate ? swiglu_far(g0, u0) : swiglu_near(g0, u0),
+                           g1 < kFarGate ? swiglu_far(g1, u1) : swiglu_near(g1, u1));
+        }
     }
     const uint32_t hm = run_max<LPG>(absmax16(hw));
     const int64_t grp = e0 / G;

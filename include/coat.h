@@ -101,6 +101,10 @@ typedef struct {
  * group_size G.   v_format  COAT_FP8_E4M3 or COAT_FP8_E5M2 (m is always E4M3).
  * hp         host pointer, read during the call only.
  * A never-updated state is codes 0, amax 0, k 1.
+ * Range: any finite moments, including groups whose max / min spans more
+ * than FP32's own ratio range (k down to about 0.064); the new moments must
+ * be finite in FP32, which bounds |g| by about sqrt(FLT_MAX / (1 - b2))
+ * (5.8e20 at b2 = 0.999).
  */
 coat_status coat_adamw_step(float *param, const uint16_t *grad_bf16,
                             uint8_t *m_codes, float *m_amax, float *m_k,

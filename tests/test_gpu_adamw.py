@@ -514,3 +514,52 @@ def test_gradients_at_the_ends_of_the_range(v_fmt):
         assert np.isfinite(gpu[0]).all() and np.isfinite(gpu[1]["v_amax"]).all()
         assert_step_parity(gpu, ref, v_fmt, f"wide gradients step {t}", prev=None if t == 1 else st)
         theta, st = ref
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+def test_narrow_groups_huge_k(v_fmt):
+    """States whose groups decode to moments within a few FP32 ulps of one
+    another (stored k of 1e5 .. 2e8), stepped with gradients that are zero or
+    far below the moments: the new k reaches 1e7 .. 1e8 and a group's codes
+    then hinge on the last ulp of each moment, so they are judged in value
+    space -- every GPU code, decoded in binary64 with the GPU's amax and k,
+    lies within the oracle group's own spread (plus 4 ulps) of the oracle's
+    moment -- beside theta parity, amax within 2 ulps, a finite positive k
+    and no NaN code.  Some groups straddle a power of two."""
+    G, n = 128, 128 * 48
+    rng = np.random.default_rng(17)
+    ng = n // G
+    theta = rng.normal(0, 0.02, n).astype(np.float32)
+    st = np_state(n, G)
+    vmax = orc.fmt_max_code(v_fmt)
+    st["m_codes"][:] = rng.integers(0x38, 0x7F, n) | (rng.integers(0, 2, n) << 7)
+    st["v_codes"][:] = rng.integers(0x38, vmax + 1, n)
+    st["m_amax"][:] = 10.0 ** rng.uniform(-4, -2, ng)
+    st["v_amax"][:] = 10.0 ** rng.uniform(-8, -5, ng)
+    # groups whose new moments (b1 m, b2 v) straddle a power of two at the first step
+    st["m_amax"][::4] = np.float32(1.0 / 0.9 * (1.0 + 6e-8))
+    st["v_amax"][1::4] = np.float32(2.0 ** -20 / 0.999 * (1.0 + 6e-8))
+    st["m_k"][:] = 10.0 ** rng.uniform(5, 8.3, ng)
+    st["v_k"][:] = 10.0 ** rng.uniform(5, 8.3, ng)
+    g = np.where(rng.random(n) < 0.5, 0.0, rng.choice([-1e-12, 1e-12], n)).astype(np.float32)
+    g_bits = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for t in (2, 3):
+        flush(f"narrow groups step {t} v={v_fmt}")
+        th_g, st_g = gpu_step(theta, g_bits, st, G, v_fmt, t)
+        ref = oracle_step(theta, g_bits, st, G, v_fmt, t, threads=1)
+        th_r, st_r = ref
+        assert_theta(th_g, th_r, f"narrow t={t} theta")
+        for name, fmt, mom in (("m", "e4m3", ref.moments[0]), ("v", v_fmt, ref.moments[1])):
+            codes, amax, k = st_g[name + "_codes"], st_g[name + "_amax"], st_g[name + "_k"]
+            assert np.isfinite(k).all() and (k > 0).all(), f"{name} t={t}: k {k.min()} .. {k.max()}"
+            assert ((codes & 0x7F) <= orc.fmt_max_code(fmt)).all(), f"{name} t={t}: NaN or inf code"
+            ar = st_r[name + "_amax"].astype(np.float64)
+            assert (np.abs(amax - ar) <= 2 * np.spacing(st_r[name + "_amax"])).all(), f"{name} t={t} amax"
+            dec = orc.expand_dequantize_groups(fmt, codes, G, amax, k)
+            m64 = mom.astype(np.float64).reshape(ng, G)
+            spread = (np.abs(m64).max(1) - np.abs(m64).min(1))[:, None]
+            err = np.abs(dec.reshape(ng, G) - m64)
+            bound = spread + 4 * np.spacing(np.abs(mom).reshape(ng, G)).astype(np.float64)
+            assert (err <= bound).all(), f"{name} t={t}: {int((err > bound).sum())} moments off"
+            assert (np.abs(m64).max(1) / np.abs(m64).min(1) < 1.0 + 2.0 ** -18).any(), "no narrow group"
+        theta, st = th_r, st_r
