@@ -171,8 +171,8 @@ __device__ __forceinline__ float run_bcast(float v) {
     return __int_as_float(r);
 }
 
-// sign(x) min(MAX (|x| / amax)^k, MAX) with the group's (amq, invq, k);
-// xs is |x| on the common path, |x| 2^sh on the prescaled one.
+// min(MAX (|x| / amax)^k, MAX) for xs = |x| with the group's (amq = amax,
+// invq, k); the caller restores the sign.
 template <int F>
 __device__ __forceinline__ float expand(float xs, float amq, float invq, float k) {
     const float r = div_rn_from_rcp(xs, amq, invq);  // RN(|x| / amax) <= 1
@@ -194,53 +194,60 @@ __device__ __forceinline__ float expand_wide(float ax, float ma, float inv_ma, i
     return __builtin_fminf(y, Fp8<F>::kMax);
 }
 
-// One wave's pass over 1024 consecutive parameters starting at `base` (wave-
-// uniform).  kTail: the last, partial chunk -- lanes past n load nothing and
-// store nothing (their whole groups are past n as well, since n % G == 0).
-template <int G, int VF, bool kTail, bool kBf16>
+// What one lane reads for its 16 parameters: master weights, gradient, both
+// moments' codes and its group's (amax, k) of each moment.
+struct ChunkIn {
+    float th[16];
+    uint32_t gw[8], mw[4], vw[4];
+    float am_m, k_m, am_v, k_v;
+};
+
+// The loads of one wave's chunk (base wave-uniform), issued without a branch
+// so that the table fill behind them waits for its own loads only.  A lane
+// with act false (past n, or in a wave with no chunk: base is then 0) reads
+// the chunk's first 16 parameters and group instead; whole groups of such
+// lanes are past n, so what they compute from it is never stored.  base + 16
+// <= n holds for every live chunk (base < n, n a multiple of 16).
+template <int G>
+__device__ __forceinline__ void load_chunk(const StepBufs &b, int64_t base, int lane, bool act, ChunkIn &in) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int LPG = G / 16;
+    const int l = act ? lane : 0;
+    const int64_t grp = base / G + l / LPG;
+    const gmem<const f32x4> *pp = reinterpret_cast<const gmem<const f32x4> *>(as_global(b.param + base)) + l * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 t = pp[i];
+        in.th[4 * i] = t.x; in.th[4 * i + 1] = t.y; in.th[4 * i + 2] = t.z; in.th[4 * i + 3] = t.w;
+    }
+    const gmem<const u32x4> *gp = reinterpret_cast<const gmem<const u32x4> *>(as_global(b.grad + base)) + l * 2;
+    const u32x4 g0 = gp[0], g1 = gp[1];
+    in.gw[0] = g0.x; in.gw[1] = g0.y; in.gw[2] = g0.z; in.gw[3] = g0.w;
+    in.gw[4] = g1.x; in.gw[5] = g1.y; in.gw[6] = g1.z; in.gw[7] = g1.w;
+    const u32x4 mc = reinterpret_cast<const gmem<const u32x4> *>(as_global(b.m_codes + base))[l];
+    const u32x4 vc = reinterpret_cast<const gmem<const u32x4> *>(as_global(b.v_codes + base))[l];
+    in.mw[0] = mc.x; in.mw[1] = mc.y; in.mw[2] = mc.z; in.mw[3] = mc.w;
+    in.vw[0] = vc.x; in.vw[1] = vc.y; in.vw[2] = vc.z; in.vw[3] = vc.w;
+    in.am_m = as_global(b.m_amax)[grp]; in.k_m = as_global(b.m_k)[grp];
+    in.am_v = as_global(b.v_amax)[grp]; in.k_v = as_global(b.v_k)[grp];
+}
+
+// One wave's pass over the 1024 consecutive parameters starting at `base`
+// (wave-uniform) whose loads load_chunk issued.  Lanes past n (act false, in
+// the last, partial chunk) store nothing; their whole groups are past n as
+// well, since n % G == 0.
+template <int G, int VF, bool kBf16>
 __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &b, const float2 *tab, int64_t base,
-                                           int lane) {
+                                           int lane, bool act, ChunkIn &in) {
     constexpr int LPG = G / 16;  // lanes per group (2 .. 64)
     const int j = lane & (LPG - 1);
     const bool v_lane = j == 1;  // lane 0 of a group computes m's parameters, lane 1 v's
-    const bool act = !kTail || base + lane * 16 < b.n;
     const int64_t gbase = base / G;  // first group of the chunk
     const int lgrp = lane / LPG;     // this lane's group within the chunk
-
-    // wave-uniform bases, per-lane constant offsets
-    const float *pth = b.param + base;
-    const uint16_t *pg = b.grad + base;
-    const uint8_t *pmc = b.m_codes + base;
-    const uint8_t *pvc = b.v_codes + base;
-
-    float th[16];
-    uint32_t gw[8], mw[4], vw[4];
-    float am_m = 0.0f, k_m = 1.0f, am_v = 0.0f, k_v = 1.0f;
-    if (act) {
-        const float4 *pp = reinterpret_cast<const float4 *>(pth) + lane * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 t = pp[i];
-            th[4 * i] = t.x; th[4 * i + 1] = t.y; th[4 * i + 2] = t.z; th[4 * i + 3] = t.w;
-        }
-        const uint4 *gp = reinterpret_cast<const uint4 *>(pg) + lane * 2;
-        const uint4 g0 = gp[0], g1 = gp[1];
-        gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
-        gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
-        const uint4 mc = reinterpret_cast<const uint4 *>(pmc)[lane];
-        const uint4 vc = reinterpret_cast<const uint4 *>(pvc)[lane];
-        mw[0] = mc.x; mw[1] = mc.y; mw[2] = mc.z; mw[3] = mc.w;
-        vw[0] = vc.x; vw[1] = vc.y; vw[2] = vc.z; vw[3] = vc.w;
-        am_m = b.m_amax[gbase + lgrp]; k_m = b.m_k[gbase + lgrp];
-        am_v = b.v_amax[gbase + lgrp]; k_v = b.v_k[gbase + lgrp];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) th[i] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gw[i] = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { mw[i] = 0u; vw[i] = 0u; }
-    }
+    float *th = in.th;
+    const uint32_t *gw = in.gw, *mw = in.mw, *vw = in.vw;
+    const float am_m = in.am_m, k_m = in.k_m, am_v = in.am_v, k_v = in.k_v;
 
     float ihm, ilm, ihv, ilv;
     recip2(k_m, ihm, ilm);
@@ -366,25 +373,48 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
 // v codes, both signs of a code byte mapping to its magnitude's entry.
 constexpr size_t kTabBytes = 512 * sizeof(float2);  // the kernels' static LDS
 
-__device__ __forceinline__ void fill_tab(float2 *tab, const StepParams &p) {
-    const uint32_t t = threadIdx.x;
-    tab[t] = p.log_tab[0][t & 127u];
-    tab[256 + t] = p.log_tab[1][t & 127u];
-    __syncthreads();
+// A thread's two table entries, read from the kernel arguments before the
+// chunk loads are issued (so waiting for them waits for nothing else) ...
+struct TabIn {
+    float2 m, v;
+};
+__device__ __forceinline__ TabIn read_tab(const StepParams &p) {
+    const uint32_t t = threadIdx.x & 127u;
+    return TabIn{p.log_tab[0][t], p.log_tab[1][t]};
 }
 
+// ... and written to LDS after.  Every thread of the workgroup takes part (the
+// barrier).  The fences order LDS only, so the chunk loads stay in flight
+// across the barrier.
+__device__ __forceinline__ void fill_tab(float2 *tab, const TabIn &e) {
+    tab[threadIdx.x] = e.m;
+    tab[256 + threadIdx.x] = e.v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A wave's chunk loads are issued first and the LDS table is filled while
+// they are in flight (measured on the 7B-shaped arena: 19.6 -> 18.6 ms, and
+// 18.4 ms with the raised issue priority).
 template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a) {
     __shared__ float2 tab[512];
-    fill_tab(tab, a.p);
     const int lane = threadIdx.x & 63;
     const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (chunk >= a.n_chunks) return;
-    if (chunk < a.buf.n / kWaveElems)  // every lane in range
-        step_chunk<G, VF, false, kBf16>(a.p, a.buf, tab, chunk * kWaveElems, lane);
-    else
-        step_chunk<G, VF, true, kBf16>(a.p, a.buf, tab, chunk * kWaveElems, lane);
+    const bool live = chunk < a.n_chunks;
+    const int64_t base = live ? chunk * kWaveElems : 0;
+    const bool act = live && base + lane * 16 < a.buf.n;
+    const TabIn te = read_tab(a.p);
+    ChunkIn in;
+    // The wave issues its loads at raised priority, ahead of older waves'
+    // arithmetic on the same SIMD, then drops back for its own.
+    __builtin_amdgcn_s_setprio(3);
+    load_chunk<G>(a.buf, base, lane, act, in);
+    __builtin_amdgcn_s_setprio(0);
+    fill_tab(tab, te);
+    if (live) step_chunk<G, VF, kBf16>(a.p, a.buf, tab, base, lane, act, in);
 }
 
 // Tensor-list form: the launch numbers the chunks of all tensors in order; a
@@ -395,25 +425,31 @@ __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a
 template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_list_kernel(const StepListArgs a) {
     __shared__ float2 tab[512];
-    fill_tab(tab, a.p);
     const int lane = threadIdx.x & 63;
     const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (chunk >= a.total_chunks) return;
-    int lo = 0, hi = a.n_tensors;  // chunk_start[lo] <= chunk < chunk_start[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.chunk_start[mid] <= chunk)
-            lo = mid;
-        else
-            hi = mid;
+    const bool live = chunk < a.total_chunks;
+    int lo = 0;
+    if (live) {
+        int hi = a.n_tensors;  // chunk_start[lo] <= chunk < chunk_start[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.chunk_start[mid] <= chunk)
+                lo = mid;
+            else
+                hi = mid;
+        }
     }
     const StepBufs b = a.entries[lo];
-    const int64_t local = chunk - a.chunk_start[lo];
-    if (local < b.n / kWaveElems)
-        step_chunk<G, VF, false, kBf16>(a.p, b, tab, local * kWaveElems, lane);
-    else
-        step_chunk<G, VF, true, kBf16>(a.p, b, tab, local * kWaveElems, lane);
+    const int64_t base = live ? (chunk - a.chunk_start[lo]) * kWaveElems : 0;
+    const bool act = live && base + lane * 16 < b.n;
+    const TabIn te = read_tab(a.p);
+    ChunkIn in;
+    __builtin_amdgcn_s_setprio(3);
+    load_chunk<G>(b, base, lane, act, in);
+    __builtin_amdgcn_s_setprio(0);
+    fill_tab(tab, te);
+    if (live) step_chunk<G, VF, kBf16>(a.p, b, tab, base, lane, act, in);
 }
 
 template <int G, int VF, bool kBf16>

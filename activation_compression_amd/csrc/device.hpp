@@ -133,6 +133,13 @@ __device__ __forceinline__ uint32_t pk_absmax_u16(uint32_t acc, uint32_t w) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Device memory seen as the global address space: the compiler then uses
+// global rather than flat memory instructions for a pointer it cannot trace to
+// a kernel argument (one read from a table in memory).  A flat load counts
+// against the LDS counter as well, so an LDS-only wait would wait for it too.
+template <class T> using gmem = __attribute__((address_space(1))) T;
+template <class T> __device__ __forceinline__ gmem<T> *as_global(T *p) { return (gmem<T> *)p; }
+
 // Correctly rounded quotient a / b from the correctly rounded reciprocal
 // y = RN(1/b): one product and one FMA-based correction (Markstein's
 // theorem; no overflow or underflow in the operands' range).
