@@ -1,6 +1,7 @@
 // abi.hip -- the C ABI of include/coat.h: argument validation, per-step
 // scalar folding and kernel dispatch.  Nothing is enqueued unless every
 // argument is valid; no device memory is allocated; no call synchronizes.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -82,10 +83,17 @@ const char *coat_status_string(coat_status s) {
 
 namespace {
 
+// eps must be a normal float so that the kernel's reciprocal of the
+// denominator sqrt(v) / sqrt(1 - b2^t) + eps >= eps stays finite (a zero
+// moment over a zero second moment is then 0, not 0 * inf); the per-step
+// factors lr / (1 - b1^t) and 1 - lr wd must be finite in FP32.
 bool valid_hparams(const coat_adamw_hparams *hp) {
     const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
-    return isfinite(lr) && isfinite(wd) && isfinite(eps) && b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0 &&
-           eps > 0.0 && hp->step >= 1;
+    if (!(isfinite(lr) && isfinite(wd) && isfinite(eps) && b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0 &&
+          eps >= (double)FLT_MIN && hp->step >= 1))
+        return false;
+    const double bc1 = 1.0 - pow(b1, (double)hp->step);
+    return isfinite((float)(lr / bc1)) && isfinite((float)(1.0 - lr * wd));
 }
 
 // Per-step scalars in binary64, rounded once.

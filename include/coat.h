@@ -53,7 +53,10 @@ typedef enum {
     COAT_ERR_SHAPE = 3,  /* n / rows / cols out of range or not divisible       */
     COAT_ERR_GROUP = 4,  /* group size not a power of two in [32, 1024]         */
     COAT_ERR_FORMAT = 5, /* unknown FP8 format                                  */
-    COAT_ERR_HPARAM = 6, /* beta outside [0,1), eps <= 0, step < 1, non-finite  */
+    COAT_ERR_HPARAM = 6, /* beta outside [0,1), eps below FLT_MIN (2^-126),
+                            step < 1, non-finite lr / wd / eps, or
+                            lr / (1 - beta1^step) or 1 - lr * wd not finite
+                            in FP32                                             */
     COAT_ERR_HIP = 7     /* the HIP runtime refused the launch                  */
 } coat_status;
 

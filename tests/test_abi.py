@@ -89,6 +89,11 @@ def test_step_rejects_bad_format_and_hparams(L):
     assert step_call(L, hparams=hp(eps=0.0)) == 6
     assert step_call(L, hparams=hp(step=0)) == 6
     assert step_call(L, hparams=hp(lr=float("nan"))) == 6
+    # eps must be normal: 1 / eps overflows FP32 below about 2.9e-39
+    assert step_call(L, hparams=hp(eps=1e-40)) == 6
+    # lr / (1 - b1^t) and 1 - lr wd must be finite in FP32
+    assert step_call(L, hparams=hp(lr=3e38)) == 6
+    assert step_call(L, hparams=hp(weight_decay=3e38, lr=10.0)) == 6
     assert L.coat_adamw_step(*([ctypes.c_void_p(FAKE)] * 8), 1024, 128, 0, None, None) == 1
 
 
