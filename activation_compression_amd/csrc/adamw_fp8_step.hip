@@ -84,8 +84,9 @@ __device__ __forceinline__ float dequant(uint32_t byte, const float2 *tab, float
 
 // The same inverse expansion for a wide group (amax = ma 2^ea, ma_ln2 = ma
 // ln2): 2^(L/k) = 2^f 2^n with n = rint(ph) and f = ph - n exact, the power
-// 2^(n + ea) applied last.  A zero code's ph is below -2^90; n is clamped at
-// -1024 so the exponent stays an int, and 2^f with f = ph + 1024 is then 0.
+// 2^(n + ea) applied last.  A zero code's ph is -2^100 / k, below -2^70 for
+// every k a group can store (k < 2^29); n is clamped at -1024 so the exponent
+// stays an int, and 2^f with f = ph + 1024 is then 0.
 template <bool kSigned>
 __device__ __forceinline__ float dequant_wide(uint32_t byte, const float2 *tab, float ma, float ma_ln2, int ea,
                                               float ih, float il) {

@@ -48,10 +48,15 @@ def step_bytes_per_param(G):
 
 
 def kernel_source_hash():
+    """Hash of the step kernel's code: its sources with comments removed and
+    runs of white space folded, so that a comment edit keeps the counters
+    taken on the same code."""
     h = hashlib.sha256()
     for f in ("adamw_fp8_step.hip", "device.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "activation_compression_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "activation_compression_amd", "csrc", f)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
