@@ -97,6 +97,9 @@ def _ptr(t: torch.Tensor | None, dtypes, name: str, numel: int | None = None):
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the launch goes to the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if numel is not None and t.numel() < numel:
