@@ -15,9 +15,10 @@
 //
 // Dequantization  x = sign(c) amax (|dec c| / MAX)^(1/k)  is evaluated as
 // amax * 2^(L(c) / k), with L(c) = log2(|dec c| / MAX) read from a 256-entry
-// LDS table (hi + lo FP32 pair per code, built per workgroup in binary64 from
-// the hardware FP8 decode) and the product L(c) / k carried in two floats, so
-// the only rounding of consequence is that of the final exp2.  A zero code's
+// LDS table (hi + lo FP32 pair per code, computed once on the host in binary64
+// from the format's field definitions, passed in the kernel arguments and
+// copied into LDS by every workgroup) and the product L(c) / k carried in two
+// floats, so the only rounding of consequence is that of the final exp2.  A zero code's
 // table entry is -2^100: 2^(-2^100 / k) is exactly 0 for every k the format
 // range can produce, so zero needs no branch.
 //
