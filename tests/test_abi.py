@@ -270,3 +270,15 @@ def test_empty_inputs_are_rejected(L):
     assert L.coat_dequant_group(f, 16, 0, 128, f, f, None) == 3
     assert L.coat_swiglu_fused(f, f, 0, 256, 128, f, f, None, None, None, None, None) == 3
     assert L.coat_group_absmax(f, 16, 0, 128, f, f, None) == 3
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libcoat.so every entry point raises before doing
+    any work (the product path has no CPU implementation to fall back to)."""
+    from activation_compression_amd import coat
+    monkeypatch.setattr(coat, "_lib", None)
+    monkeypatch.setattr(coat, "LIB_PATH", str(tmp_path / "libcoat.so"))
+    with pytest.raises(coat.CoatError, match="missing"):
+        coat.lib()
+    with pytest.raises(coat.CoatError, match="missing"):
+        coat.status_string(0)
