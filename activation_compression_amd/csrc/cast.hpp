@@ -49,12 +49,19 @@ __device__ __forceinline__ CastQ cast_q(float a) {
 // E4M3 codes of 16 BF16 values.  448 (x 2^sh) is exact -- a BF16 value in
 // [-2, 2] times 7 * 2^6 has at most 11 significant bits -- and neither factor
 // leaves the FP32 range for any finite BF16 slice, however large or small.
+// kAnyScale: a may be below max |x| (a scale the caller supplies); x 2^sh is
+// then clamped to +-2^100 first, which saturates all the same, so that the
+// product cannot overflow to infinity and the quotient's correction cannot
+// turn it into NaN.
+template <bool kAnyScale = false>
 __device__ __forceinline__ uint4 cast16(const uint32_t w[8], const CastQ &q) {
     float y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float x = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-        const float t = div_rn_from_rcp(__builtin_amdgcn_ldexpf(x, q.sh) * q.m448, q.a_s, q.inv_s);
+        float xs = __builtin_amdgcn_ldexpf(x, q.sh);
+        if constexpr (kAnyScale) xs = __builtin_amdgcn_fmed3f(xs, -0x1p100f, 0x1p100f);
+        const float t = div_rn_from_rcp(xs * q.m448, q.a_s, q.inv_s);
         y[i] = __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
     }
     return make_uint4(cvt4<kE4M3>(y[0], y[1], y[2], y[3]), cvt4<kE4M3>(y[4], y[5], y[6], y[7]),

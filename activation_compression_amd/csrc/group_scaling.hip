@@ -96,13 +96,13 @@ __global__ __launch_bounds__(kBlock) void quant_per_tensor_kernel(const uint16_t
         if (e0 + 16 <= n) {
             uint32_t w[8];
             load16(x + e0, w);
-            *reinterpret_cast<uint4 *>(codes + e0) = cast16(w, q);
+            *reinterpret_cast<uint4 *>(codes + e0) = cast16<true>(w, q);
         } else if (e0 < n) {  // n % 16 == 8: the last lane holds 8 values
             uint32_t w[8];
             const uint4 a = reinterpret_cast<const uint4 *>(x + e0)[0];
             w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
             w[4] = w[5] = w[6] = w[7] = 0u;
-            const uint4 c = cast16(w, q);
+            const uint4 c = cast16<true>(w, q);
             *reinterpret_cast<uint2 *>(codes + e0) = make_uint2(c.x, c.y);
         }
     }

@@ -212,7 +212,9 @@ coat_status coat_absmax_reduce(const float *partial, int64_t n, float *amax, voi
  *   A = *amax (device scalar, e.g. from coat_group_absmax, read on device);
  *   code = RNE_sat(y) with y the FP32 value of 448 * x / A (correctly
  *   rounded quotient); *scale = FP32(A / 448), the dequantization scale.
- *   A = 0 gives scale 1 and all codes 0.
+ *   A = 0 gives scale 1 and all codes 0.  A need not be max |x| (a scale
+ *   kept from an earlier step, say): larger values saturate to +-448, also
+ *   where 448 x / A exceeds FP32.
  *
  * x_bf16  BF16 [n], read only.  16-byte aligned.  n > 0, a multiple of 8.
  * amax    FP32 [1] device scalar, read only.

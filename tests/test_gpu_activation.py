@@ -457,3 +457,28 @@ def test_per_tensor_cast_at_the_ends_of_the_bf16_range(scale):
     torch.cuda.synchronize()
     rc, rs = orc.quant_per_tensor(x, A)
     assert host(sc)[0] == rs and (norm0(host(codes)) == rc).all()
+
+
+@pytest.mark.parametrize("case", ["quarter", "hundredfold", "far-below", "denormal"])
+def test_per_tensor_cast_with_a_supplied_scale(case):
+    """The per-tensor cast takes its absmax from the caller (for instance one
+    kept from an earlier step), so A need not be the tensor's max: values
+    beyond it saturate to +-448, also where 448 x / A leaves FP32 altogether
+    (never a NaN code), and values far below it go to 0.  Bit-exact."""
+    g = torch.Generator().manual_seed(7)
+    t = torch.randn(64, 1032, generator=g)
+    t[3, :40] *= 1e4
+    big = case in ("far-below", "denormal")
+    x = _bf16_of(t * (1e28 if big else 1.0)).reshape(-1)
+    mx = float(np.abs((x.astype(np.uint32) << 16).view(np.float32)).max())
+    A = np.float32({"quarter": mx / 4, "hundredfold": mx * 100, "far-below": mx * 1e-60,
+                    "denormal": 1e-40}[case])
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, device="cuda")
+    flush(f"per-tensor cast, supplied scale {case} (A = {A:.3e}, max {mx:.3e})")
+    coat.coat_quant_per_tensor(dev(x), torch.tensor([A], device="cuda"), codes, sc)
+    torch.cuda.synchronize()
+    rc, rs = orc.quant_per_tensor(x, A)
+    assert ((rc & 0x7F) != 0x7F).all()
+    got = norm0(host(codes))
+    assert host(sc)[0] == rs and (got == rc).all(), f"{case}: {int((got != rc).sum())} codes differ"
