@@ -103,7 +103,8 @@ typedef struct {
  *            passed as one flat arena (one launch for the whole model).
  * group_size G.   v_format  COAT_FP8_E4M3 or COAT_FP8_E5M2 (m is always E4M3).
  * hp         host pointer, read during the call only.
- * A never-updated state is codes 0, amax 0, k 1.
+ * A never-updated state is codes 0, amax 0, k 1; any other state must be
+ * one a previous call wrote (or a byte copy of it: a checkpoint).
  * Range: any finite moments, including groups whose max / min spans more
  * than FP32's own ratio range (k down to about 0.064); the new moments must
  * be finite in FP32, which bounds |g| by about sqrt(FLT_MAX / (1 - b2))
