@@ -34,8 +34,12 @@ def golden_rows(name):
 
 
 def pytest_sessionfinish(session, exitstatus):
-    """Write the measured code-mismatch counts of the GPU parity tests next to
-    the other GPU run outputs (only when a GPU run produced some)."""
+    """Write the measured code-mismatch counts of the GPU parity tests as JSON
+    to the path in COAT_PARITY_STATS, when it is set and a GPU run produced
+    some."""
+    path = os.environ.get("COAT_PARITY_STATS")
+    if not path:
+        return
     try:
         import parity
     except Exception:
@@ -43,11 +47,10 @@ def pytest_sessionfinish(session, exitstatus):
     if not parity.STATS and not parity.BF16_STATS:
         return
     import json
-    out = os.path.join(ROOT, "gpurun_out")
-    os.makedirs(out, exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     tot_n = sum(r[1] for r in parity.STATS)
     tot_bad = sum(r[2] for r in parity.STATS)
-    with open(os.path.join(out, "parity_code_stats.json"), "w") as f:
+    with open(path, "w") as f:
         json.dump({"elements_compared": tot_n, "mismatching_codes": tot_bad,
                    "mismatch_fraction": tot_bad / max(tot_n, 1),
                    "max_grid_steps": max((r[3] for r in parity.STATS), default=0),
