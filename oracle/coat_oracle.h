@@ -22,7 +22,11 @@
  * Parity status: every function here is pinned by the CPU tests (codec brute
  * force and page constants, the E2M2 worked grid, the k = 1 reduction, the
  * expansion invariants and error bound, AdamW against torch.optim.AdamW, the
- * step-1 closed form, Group Scaling against torch.amax and torch's FP8 casts).
+ * step-1 closed form, Group Scaling against torch.amax and torch's FP8 casts,
+ * BF16 rounding against torch's cast, dequantization against torch's E4M3
+ * decode times the scale, SwiGLU against torch's float64 silu, RMSNorm against
+ * torch's float64 rms_norm and its closed forms), and the pins are checked by
+ * planting mistakes in a copy of this oracle.
  * The 1.63x quantization-error figure of [COAT] is "parity unpinned": it needs
  * real optimizer states that are not available.
  */
