@@ -298,17 +298,20 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
         mn_m = min(mn_m, (__float_as_uint(m) << 1) - 2u);
         mn_v = min(mn_v, (__float_as_uint(v) << 1) - 2u);
     }
+    // Stores go through global-address-space pointers (as the loads do): a flat
+    // store counts against the LDS counter too, and the group reductions below
+    // would then wait for it.
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     if (act) {
-        float4 *pp = reinterpret_cast<float4 *>(b.param + base) + lane * 4;
+        gmem<f32x4> *pp = reinterpret_cast<gmem<f32x4> *>(as_global(b.param + base)) + lane * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            pp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
+        for (int i = 0; i < 4; ++i) pp[i] = f32x4{th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]};
         if constexpr (kBf16) {  // the working copy the next forward pass reads
-            uint4 *bp = reinterpret_cast<uint4 *>(b.param_bf16 + base) + lane * 2;
-            bp[0] = make_uint4(bf16x2(th[0], th[1]), bf16x2(th[2], th[3]), bf16x2(th[4], th[5]),
-                               bf16x2(th[6], th[7]));
-            bp[1] = make_uint4(bf16x2(th[8], th[9]), bf16x2(th[10], th[11]), bf16x2(th[12], th[13]),
-                               bf16x2(th[14], th[15]));
+            gmem<u32x4> *bp = reinterpret_cast<gmem<u32x4> *>(as_global(b.param_bf16 + base)) + lane * 2;
+            bp[0] = u32x4{bf16x2(th[0], th[1]), bf16x2(th[2], th[3]), bf16x2(th[4], th[5]), bf16x2(th[6], th[7])};
+            bp[1] = u32x4{bf16x2(th[8], th[9]), bf16x2(th[10], th[11]), bf16x2(th[12], th[13]),
+                          bf16x2(th[14], th[15])};
         }
     }
 
@@ -322,8 +325,8 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
     const GroupQ q = group_q(v_lane ? gx_v : gx_m, v_lane ? gn_v : gn_m,
                              v_lane ? p.v_log2_range : p.m_log2_range);
     if (act && j < 2) {
-        (v_lane ? b.v_amax : b.m_amax)[gbase + lgrp] = q.amax;
-        (v_lane ? b.v_k : b.m_k)[gbase + lgrp] = q.k;
+        as_global(v_lane ? b.v_amax : b.m_amax)[gbase + lgrp] = q.amax;
+        as_global(v_lane ? b.v_k : b.m_k)[gbase + lgrp] = q.k;
     }
     const float amq_m = run_bcast<LPG, 0>(q.amq), inv_m = run_bcast<LPG, 0>(q.invq);
     const float kq_m = run_bcast<LPG, 0>(q.k);
@@ -366,8 +369,8 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
         }
     }
     if (act) {
-        reinterpret_cast<uint4 *>(b.m_codes + base)[lane] = make_uint4(om[0], om[1], om[2], om[3]);
-        reinterpret_cast<uint4 *>(b.v_codes + base)[lane] = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+        reinterpret_cast<gmem<u32x4> *>(as_global(b.m_codes + base))[lane] = u32x4{om[0], om[1], om[2], om[3]};
+        reinterpret_cast<gmem<u32x4> *>(as_global(b.v_codes + base))[lane] = u32x4{ov[0], ov[1], ov[2], ov[3]};
     }
 }
 
