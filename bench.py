@@ -456,6 +456,8 @@ def main():
     elems = {"adamw_fp8_step": n, "group_absmax": acts[0].numel, "quant_per_tensor": acts[0].numel,
              "quant_group_linear": acts[0].numel, "quant_group_swiglu": acts[1].numel}
     kernels = {nm: entry(alg[nm], per[nm], elems[nm]) for nm in names}
+    kernels["group_absmax"]["note"] = ("runs right after the optimizer step and shares HBM with the write-back "
+                                       "of the step's last dirty cache lines")
     step_ms = sorted(m[0].elapsed_time(m[5]) for m in marks)
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * sum(step_ms[len(step_ms) // 2 - 1:][:2])
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
