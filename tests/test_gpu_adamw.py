@@ -614,3 +614,50 @@ def test_three_hundred_steps_with_persistent_gradients(v_fmt):
     gpu = gpu_step(th, g_bits, st, G, v_fmt, T + 1)
     ref = oracle_step(th, g_bits, st, G, v_fmt, T + 1)
     assert_step_parity(gpu, ref, v_fmt, f"step {T + 1} after 300 free-running steps", prev=st)
+
+
+def test_concurrent_calls_from_two_threads_on_two_streams():
+    """The ABI allows concurrent calls on disjoint buffers from any host
+    thread: two threads, each with its own (default-priority) stream and its
+    own 1 Mi-parameter problem, twenty steps each, running at the same time.
+    Every byte equals a sequential run of the same problems on the default
+    stream."""
+    import threading
+
+    G, n, T = 128, 1 << 20, 20
+    rng = np.random.default_rng(31)
+    thetas = [rng.normal(0, 0.02, n).astype(np.float32) for _ in range(2)]
+    grads = [[torch.from_numpy((rng.normal(0, 1e-3, n) * np.exp(rng.normal(0, 1, n))).astype(np.float32))
+              .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16) for _ in range(T)] for _ in range(2)]
+
+    def run(i, stream, out, err):
+        try:
+            with torch.cuda.stream(stream):
+                th = dev(thetas[i])
+                st = {k: dev(v) for k, v in np_state(n, G).items()}
+                gs = [dev(g) for g in grads[i]]
+                for t in range(T):
+                    coat.coat_adamw_step(th, gs[t], st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"],
+                                         st["v_amax"], st["v_k"], group_size=G, v_format=("e4m3", "e5m2")[i],
+                                         hp=gpu_hp(t + 1), stream=stream)
+                stream.synchronize()
+                out[i] = (host(th), {k: host(v) for k, v in st.items()})
+        except Exception as e:  # surfaced in the main thread
+            err.append(e)
+
+    flush("two threads, two streams")
+    conc, err = [None, None], []
+    threads = [threading.Thread(target=run, args=(i, torch.cuda.Stream(), conc, err)) for i in range(2)]
+    for th_ in threads:
+        th_.start()
+    for th_ in threads:
+        th_.join()
+    assert not err, err
+    seq = [None, None]
+    for i in range(2):
+        run(i, torch.cuda.current_stream(), seq, err)
+    assert not err, err
+    for i in range(2):
+        assert (conc[i][0].view(np.uint32) == seq[i][0].view(np.uint32)).all()
+        for k in STATE_KEYS:
+            assert (conc[i][1][k].view(np.uint8) == seq[i][1][k].view(np.uint8)).all(), (i, k)
