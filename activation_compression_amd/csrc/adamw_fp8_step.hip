@@ -18,9 +18,14 @@
 // LDS table (hi + lo FP32 pair per code, computed once on the host in binary64
 // from the format's field definitions, passed in the kernel arguments and
 // copied into LDS by every workgroup) and the product L(c) / k carried in two
-// floats, so the only rounding of consequence is that of the final exp2.  A zero code's
-// table entry is -2^100: 2^(-2^100 / k) is exactly 0 for every k the format
-// range can produce, so zero needs no branch.
+// floats, so the only rounding of consequence is that of the final exp2.  A
+// zero code's table entry is Z = -2^40, so zero needs no branch: 2^(Z / k) is
+// exactly 0 for every k the step stores (k < 2^29), and the correction term
+// Z (1/k)_lo stays below 2^21 in magnitude (|(1/k)_lo| <= 2^-23 / k, k >=
+// 0.13 on this form), so the factor amax (1 + ln2 pl) it multiplies is finite
+// for amax <= 2^100 and the product is 0, as the expansion maps zero to zero
+// (sign(0) = 0).  Groups with a larger amax take the wide form below, whose
+// factor has amax's mantissa in place of amax.
 //
 // Requantization  c = RNE_sat(sign(x) MAX (|x| / amax)^k)  forms the ratio
 // |x| / amax correctly rounded (RN reciprocal and one Markstein correction),
@@ -37,9 +42,10 @@
 // amax = ma 2^ea split exactly (frexp), log2(|x| / amax) = (ex - ea) +
 // log2(mx / ma) with the mantissa quotient correctly rounded in (1/2, 2); and
 // dequantization splits 2^(L/k) = 2^f 2^n (n = rint(L/k), exact) and applies
-// 2^(n + ea) last with ldexp.  Such groups are rare (gradients spanning
-// dozens of decades within G values), so the branch is taken by whole lanes
-// and costs the common path a compare.
+// 2^(n + ea) last with ldexp; dequantization also takes this form for a
+// group stored with amax above 2^100.  Such groups are rare (gradients
+// spanning dozens of decades within G values, or moments beyond 1e30), so the
+// branch is taken by whole lanes and costs the common path a compare.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -85,9 +91,10 @@ __device__ __forceinline__ float dequant(uint32_t byte, const float2 *tab, float
 
 // The same inverse expansion for a wide group (amax = ma 2^ea, ma_ln2 = ma
 // ln2): 2^(L/k) = 2^f 2^n with n = rint(ph) and f = ph - n exact, the power
-// 2^(n + ea) applied last.  A zero code's ph is -2^100 / k, below -2^70 for
+// 2^(n + ea) applied last.  A zero code's ph is -2^40 / k, below -2^11 for
 // every k a group can store (k < 2^29); n is clamped at -1024 so the exponent
-// stays an int, and 2^f with f = ph + 1024 is then 0.
+// stays an int, and 2^f with f = ph + 1024 is then 0.  The factor beside it
+// stays finite: ma < 1 and |pl| < 2^22 (1/k <= 16 here).
 template <bool kSigned>
 __device__ __forceinline__ float dequant_wide(uint32_t byte, const float2 *tab, float ma, float ma_ln2, int ea,
                                               float ih, float il) {
@@ -104,9 +111,13 @@ __device__ __forceinline__ float dequant_wide(uint32_t byte, const float2 *tab, 
     return mag;
 }
 
-// A stored group the fast dequantization cannot reproduce: 2^(L/k) for the
-// smallest nonzero code, 2^(-log2 R_fmt / k), would pass 2^-120.
-__device__ __forceinline__ bool wide_k(float k, float log2_range) { return k * 120.0f < log2_range; }
+// A stored group the fast dequantization cannot take: 2^(L/k) for the
+// smallest nonzero code, 2^(-log2 R_fmt / k), would pass 2^-120, or amax is
+// above 2^100 (a zero code's correction term could then overflow the factor
+// amax (1 + ln2 pl)).
+__device__ __forceinline__ bool wide_group(float k, float amax, float log2_range) {
+    return k * 120.0f < log2_range || amax > 0x1p100f;
+}
 
 // Per-group quantization parameters of one new moment.
 struct GroupQ {
@@ -257,7 +268,7 @@ __device__ __forceinline__ void step_chunk(const StepParams &p, const StepBufs &
 
     // dequantize the old moments into m1 / v1 (a lane's groups decide its path)
     float m1[16], v1[16];
-    if (!(wide_k(k_m, p.m_log2_range) || wide_k(k_v, p.v_log2_range))) {
+    if (!(wide_group(k_m, am_m, p.m_log2_range) || wide_group(k_v, am_v, p.v_log2_range))) {
         const float am_m_ln2 = am_m * kLn2, am_v_ln2 = am_v * kLn2;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -499,7 +510,7 @@ static void build_log_table(int fmt, float2 *tab) {
         const int e = c >> mbits, m = c & ((1 << mbits) - 1);
         const bool special = fmt == kE5M2 ? e == 31 : (e == 15 && m == 7);
         if (c == 0 || special) {
-            tab[c] = make_float2(-0x1p100f, 0.0f);  // 2^(-2^100 / k) is exactly 0
+            tab[c] = make_float2(-0x1p40f, 0.0f);  // 2^(-2^40 / k) is exactly 0 for every stored k
             continue;
         }
         const double d = e == 0 ? ldexp((double)m, 1 - bias - mbits)

@@ -32,7 +32,7 @@ struct StepParams {
     float m_log2_range;   // log2(MAX / smallest subnormal) of m's format
     float v_log2_range;   // ... of v's format
     // log2(|decode(c)| / MAX) for every code magnitude c, as an FP32 hi + lo
-    // pair (code 0 and non-finite codes hold -2^100): m's format, then v's.
+    // pair (code 0 and non-finite codes hold -2^40): m's format, then v's.
     float2 log_tab[2][128];
 };
 

@@ -516,6 +516,51 @@ def test_gradients_at_the_ends_of_the_range(v_fmt):
         theta, st = ref
 
 
+def narrow_large_grads(n, G, rng):
+    """Per group: |g| = 10^(c + w u), u uniform in [-1/2, 1/2], with centre c
+    uniform in [9, 11] (a quarter of the groups at c = 18) and width w from
+    0.02 to 2 decades, random signs, 5% exact zeros."""
+    ng = n // G
+    c = np.where(rng.random(ng) < 0.25, 18.0, rng.uniform(9.0, 11.0, ng))
+    w = 10.0 ** rng.uniform(np.log10(0.02), np.log10(2.0), ng)
+    mag = 10.0 ** (np.repeat(c, G) + np.repeat(w, G) * rng.uniform(-0.5, 0.5, n))
+    g = mag * rng.choice([-1.0, 1.0], n)
+    g[rng.random(n) < 0.05] = 0.0
+    return torch.from_numpy(g.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("G", [32, 128, 1024])
+def test_narrow_large_groups_with_exact_zeros(v_fmt, G):
+    """Groups of large, narrow moments holding exact zeros: |g| around 1e9 ..
+    1e11 (v around 1e15 .. 1e19) and 1e18 (m around 1e17, v beyond 2^100),
+    two lockstep steps.  At step 2 the zero codes of these groups are decoded
+    with a large amax and k of a few -- where a zero code once decoded to NaN
+    -- and must give 0: the expansion maps zero to zero (COAT explainer,
+    "expansion function").  Every output finite, and the step's parity bar
+    against the oracle."""
+    n = 1024 * 64
+    rng = np.random.default_rng(41 + G)
+    theta = rng.normal(0, 0.02, n).astype(np.float32)
+    st = np_state(n, G)
+    for t in (1, 2):
+        g = narrow_large_grads(n, G, rng)
+        if t == 2:
+            # the regime of the old failure is present in the state being decoded
+            zero_codes = ((st["v_codes"] & 0x7F) == 0).reshape(-1, G).any(axis=1)
+            assert (zero_codes & (st["v_amax"] > 1e16) & (st["v_k"] > 2)).any()
+            zero_m = ((st["m_codes"] & 0x7F) == 0).reshape(-1, G).any(axis=1)
+            assert (zero_m & (st["m_amax"] > 1e16) & (st["m_k"] > 2)).any()
+        flush(f"narrow large groups step {t} G={G} v={v_fmt}")
+        gpu = gpu_step(theta, g, st, G, v_fmt, t)
+        ref = oracle_step(theta, g, st, G, v_fmt, t)
+        assert np.isfinite(gpu[0]).all()
+        for k in ("m_amax", "m_k", "v_amax", "v_k"):
+            assert np.isfinite(gpu[1][k]).all(), k
+        assert_step_parity(gpu, ref, v_fmt, f"narrow large t={t} G={G}", prev=st)
+        theta, st = ref
+
+
 @pytest.mark.parametrize("v_fmt", ["e4m3", "e5m2"])
 def test_narrow_groups_huge_k(v_fmt):
     """States whose groups decode to moments within a few FP32 ulps of one
