@@ -58,6 +58,11 @@ def lib():
     L.orc_expand_quantize.argtypes = [i32, P, i64, f64, P, P, P]
     L.orc_expand_quantize.restype = None
     L.orc_expand_dequantize.argtypes, L.orc_expand_dequantize.restype = [i32, u32, f32, f32], f64
+    L.orc_expand_encode.argtypes, L.orc_expand_encode.restype = [i32, f64, f32, f32], u32
+    L.orc_expand_encode_each.argtypes = [i32, P, P, P, i64, P]
+    L.orc_expand_encode_each.restype = None
+    L.orc_expand_encode_groups.argtypes = [i32, P, i64, i64, i64, P, P, P]
+    L.orc_expand_encode_groups.restype = None
     L.orc_expand_quantize_groups.argtypes = [i32, P, i64, i64, i64, P, P, P, P]
     L.orc_expand_quantize_groups.restype = None
     L.orc_expand_dequantize_groups.argtypes = [i32, P, i64, i64, i64, P, P, P]
@@ -159,6 +164,34 @@ def expand_quantize_groups(fmt, x, G: int, k_given=None, threads: int = 1):
 
     _run_blocks(run, _row_blocks(ng, threads), threads)
     return codes, amax, k
+
+
+def expand_encode_groups(fmt, x, G: int, amax, k, threads: int = 1) -> np.ndarray:
+    """The code of every value of x (binary64) in its group stored with the
+    given (amax, k) (float32 per group): the quantizer's last step alone."""
+    xx = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    kk = np.ascontiguousarray(k, dtype=np.float32)
+    codes = np.zeros(xx.size, dtype=np.uint8)
+    L = lib()
+    f = fmt_id(fmt)
+
+    def run(lo, hi):
+        L.orc_expand_encode_groups(f, _ptr(xx), lo, hi, G, _ptr(a), _ptr(kk), _ptr(codes))
+
+    _run_blocks(run, _row_blocks(xx.size // G, threads), threads)
+    return codes
+
+
+def expand_encode_each(fmt, x, amax, k) -> np.ndarray:
+    """The code of every x[i] (binary64) in a group stored with (amax[i], k[i])."""
+    xx = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    kk = np.ascontiguousarray(k, dtype=np.float32)
+    assert a.size == xx.size and kk.size == xx.size
+    codes = np.zeros(xx.size, dtype=np.uint8)
+    lib().orc_expand_encode_each(fmt_id(fmt), _ptr(xx), _ptr(a), _ptr(kk), xx.size, _ptr(codes))
+    return codes
 
 
 def expand_dequantize_groups(fmt, codes, G: int, amax, k, threads: int = 1) -> np.ndarray:

@@ -202,18 +202,38 @@ void orc_expand_quantize(int fmt, const float *x, int64_t G, double k_force,
     else
         k = (float)(log(r_fmt) / log(amax / amin));
 
-    for (i = 0; i < G; ++i) {
-        double xi = (double)x[i];
-        if (xi == 0.0) {
-            codes[i] = 0;
-            continue;
-        }
-        double y = vmax * pow(fabs(xi) / amax, (double)k);
-        float y32 = (float)y;
-        codes[i] = (uint8_t)orc_fp8_encode(fmt, xi < 0 ? -(double)y32 : (double)y32);
-    }
+    for (i = 0; i < G; ++i)
+        codes[i] = (uint8_t)orc_expand_encode(fmt, (double)x[i], (float)amax, k);
     *amax_out = (float)amax; /* amax is an FP32 value, so this is exact */
     *k_out = k;
+}
+
+/* The last step of the group quantization on its own: the code of a value x
+ * in a group stored with (amax, k), RNE_sat(sign(x) * MAX * (|x| / amax)^k)
+ * with the power's value rounded to FP32 first.  x = 0 (or amax = 0) gives
+ * code 0.  x need not be an FP32 value. */
+uint32_t orc_expand_encode(int fmt, double x, float amax, float k)
+{
+    if (x == 0.0 || amax == 0.0f)
+        return 0u;
+    double y = orc_fp8_max(fmt) * pow(fabs(x) / (double)amax, (double)k);
+    float y32 = (float)y;
+    return orc_fp8_encode(fmt, x < 0 ? -(double)y32 : (double)y32);
+}
+
+void orc_expand_encode_each(int fmt, const double *x, const float *amax, const float *k, int64_t n,
+                            uint8_t *codes)
+{
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = (uint8_t)orc_expand_encode(fmt, x[i], amax[i], k[i]);
+}
+
+void orc_expand_encode_groups(int fmt, const double *x, int64_t g0, int64_t g1, int64_t G,
+                              const float *amax, const float *k, uint8_t *codes)
+{
+    for (int64_t g = g0; g < g1; ++g)
+        for (int64_t i = 0; i < G; ++i)
+            codes[g * G + i] = (uint8_t)orc_expand_encode(fmt, x[g * G + i], amax[g], k[g]);
 }
 
 void orc_expand_quantize_groups(int fmt, const float *x, int64_t g0, int64_t g1, int64_t G,

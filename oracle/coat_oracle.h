@@ -74,6 +74,18 @@ void orc_expand_quantize(int fmt, const float *x, int64_t G, double k_force,
 void orc_expand_quantize_groups(int fmt, const float *x, int64_t g0, int64_t g1, int64_t G,
                                 const float *k_given, uint8_t *codes, float *amax, float *k);
 
+/* The code of a value x (any binary64 value) in a group stored with (amax,
+ * k): the last step of orc_expand_quantize on its own. */
+uint32_t orc_expand_encode(int fmt, double x, float amax, float k);
+
+/* orc_expand_encode of x[i] with its own (amax[i], k[i]), i < n. */
+void orc_expand_encode_each(int fmt, const double *x, const float *amax, const float *k, int64_t n,
+                            uint8_t *codes);
+
+/* orc_expand_encode of every x of groups [g0, g1) with its group's (amax, k). */
+void orc_expand_encode_groups(int fmt, const double *x, int64_t g0, int64_t g1, int64_t G,
+                              const float *amax, const float *k, uint8_t *codes);
+
 /* Inverse expansion of one code with its group's stored (amax, k). */
 double orc_expand_dequantize(int fmt, uint32_t code, float amax, float k);
 

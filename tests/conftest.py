@@ -48,13 +48,18 @@ def pytest_sessionfinish(session, exitstatus):
         return
     import json
     os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
-    tot_n = sum(r[1] for r in parity.STATS)
-    tot_bad = sum(r[2] for r in parity.STATS)
+    tot_n = sum(r["n"] for r in parity.STATS)
+    tot_bad = sum(r["own_mismatches"] for r in parity.STATS)
+    rule_n = sum(r["rule_n"] for r in parity.STATS)
+    rule_bad = sum(r["rule_mismatches"] for r in parity.STATS)
     with open(path, "w") as f:
-        json.dump({"elements_compared": tot_n, "mismatching_codes": tot_bad,
+        json.dump({"elements_compared": tot_n, "mismatches_vs_oracle_codes": tot_bad,
                    "mismatch_fraction": tot_bad / max(tot_n, 1),
-                   "max_grid_steps": max((r[3] for r in parity.STATS), default=0),
-                   "per_comparison": [{"what": w, "n": n, "mismatches": b, "max_grid_steps": st}
-                                      for w, n, b, st in parity.STATS],
+                   "max_grid_steps_vs_oracle_codes": max((r["own_max_steps"] for r in parity.STATS), default=0),
+                   "rule_elements": rule_n, "rule_mismatches": rule_bad,
+                   "rule_mismatch_fraction": rule_bad / max(rule_n, 1),
+                   "rule_max_grid_steps": max((r["rule_max_steps"] for r in parity.STATS), default=0),
+                   "amax_max_ulps": max((r["amax_max_ulps"] for r in parity.STATS), default=0),
+                   "per_comparison": parity.STATS,
                    "bf16_outputs": [{"what": w, "n": n, "not_identical": b, "not_identical_fraction": b / max(n, 1)}
                                     for w, n, b in parity.BF16_STATS]}, f, indent=1)

@@ -152,3 +152,33 @@ def test_wide_group_gets_k_below_one(orc):
         codes, amax, k = orc.expand_quantize(fmt, x)
         assert 0 < k < 1
         assert (codes[x == np.float32(1e-8)] & 0x7F == 1).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_with_given_scale_and_k(orc, fmt):
+    """The quantizer's last step on its own (orc_expand_encode): with a group's
+    own stored (amax, k) it gives the group's codes; the stored max maps to
+    the largest code, amax (min_sub / MAX)^(1/k) to the smallest subnormal
+    code, zero to zero, and the sign is carried; with k = 1 it is the plain
+    absmax cast of a value that need not be FP32."""
+    rng = np.random.default_rng(23)
+    G = 128
+    x = random_groups(rng, 40, G, 5, zero_frac=0.05)
+    codes, amax, k = orc.expand_quantize_groups(fmt, x.ravel(), G)
+    again = orc.expand_encode_groups(fmt, x.ravel().astype(np.float64), G, amax, k)
+    assert (again == codes).all()
+    top, mx, ms = orc.fmt_max_code(fmt), orc.fmt_max(fmt), orc.fmt_min_subnormal(fmt)
+    a = np.float32(3.0e-5)
+    for kk in (0.3, 1.0, 2.5, 9.0):
+        kf = np.float32(kk)
+        lo = float(a) * (ms / mx) ** (1.0 / float(kf))
+        got = orc.expand_encode_groups(fmt, np.array([float(a), -float(a), lo, -lo, 0.0, 0.0] + [0.0] * (G - 6)), G,
+                                       np.array([a], np.float32), np.array([kf], np.float32))
+        assert list(got[:5]) == [top, 0x80 | top, 1, 0x81, 0]
+    # k = 1: RNE_sat(MAX x / amax) of binary64 x, e.g. a midpoint between two codes
+    c = 0x30 if fmt == "e4m3" else 0x30
+    mid = 0.5 * (orc.decode(fmt, c) + orc.decode(fmt, c + 1))
+    want = orc.encode(fmt, float(np.float32(mid)))
+    got = orc.expand_encode_groups(fmt, np.array([mid * float(a) / mx] + [0.0] * (G - 1)), G,
+                                   np.array([a], np.float32), np.array([1.0], np.float32))
+    assert got[0] == want
