@@ -196,11 +196,15 @@ def moment_bounds(ref, prev, threads=THREADS):
     G, v_fmt = ref.G, ref.v_fmt
 
     def old(name, fmt, e0, e1):
+        # |old moment| for the bound: amax (|dec c| / MAX)^(1/k), with the oracle's decoding of the codes
         if prev is None:
             return np.zeros(e1 - e0)
         g0, g1 = e0 // G, e1 // G
-        return np.abs(orc.expand_dequantize_groups(fmt, prev[name + "_codes"].reshape(-1)[e0:e1], G,
-                                                   prev[name + "_amax"][g0:g1], prev[name + "_k"][g0:g1]))
+        mag = decode_table(fmt)[prev[name + "_codes"].reshape(-1)[e0:e1] & 0x7F].reshape(-1, G)
+        amax = prev[name + "_amax"][g0:g1].astype(np.float64)[:, None]
+        k = prev[name + "_k"][g0:g1].astype(np.float64)[:, None]
+        with np.errstate(divide="ignore"):
+            return (amax * (mag / FMT_MAX[fmt]) ** (1.0 / k)).ravel()
 
     def grad(e0, e1):
         return _bf16_f64(ref.grad_bits.reshape(-1)[e0:e1])
@@ -218,6 +222,36 @@ def moment_bounds(ref, prev, threads=THREADS):
         return bound(t, np.abs(ref.moments[1].reshape(-1)[e0:e1].astype(np.float64)))
 
     return dm, dv
+
+
+FMT_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+_CELLS = {}
+_DECODE = {}
+
+
+def decode_table(fmt):
+    """|decode(c)| of every code magnitude (0 for codes the step never writes)."""
+    if fmt not in _DECODE:
+        top = orc.fmt_max_code(fmt)
+        _DECODE[fmt] = np.array([orc.decode(fmt, c) if c <= top else 0.0 for c in range(128)])
+    return _DECODE[fmt]
+
+
+def cell_bounds(fmt):
+    """(lower, upper) rounding boundaries of every code magnitude: the
+    midpoints between neighbouring grid values of the oracle's codec (0 below
+    code 1's cell ... infinity above the largest code, which saturates)."""
+    if fmt not in _CELLS:
+        top = orc.fmt_max_code(fmt)
+        grid = np.array([orc.decode(fmt, c) for c in range(top + 1)])
+        lo = np.full(256, np.inf)
+        hi = np.full(256, -np.inf)
+        lo[0], hi[0] = 0.0, 0.5 * grid[1]
+        for c in range(1, top + 1):
+            lo[c] = 0.5 * (grid[c - 1] + grid[c])
+            hi[c] = 0.5 * (grid[c] + grid[c + 1]) if c < top else np.inf
+        _CELLS[fmt] = (lo, hi)
+    return _CELLS[fmt]
 
 
 def _judge_chunk(c, g0, g1):
@@ -288,7 +322,7 @@ def _judge_chunk(c, g0, g1):
 
     # the oracle's own codes on the elements whose code the update's FP32 error cannot move: with
     # y = MAX (|x| / amax)^k, |d ln y| <= k (rho + rho_max) + |ln r| k sigma =: dl; the element is in the
-    # rule set when |x| scaled so that y moves by e^(-dl) and e^(dl) still encodes to the oracle's code
+    # rule set when y e^(-dl) and y e^(dl) still round to the oracle's code
     k_o = c["ref_k"][g0:g1].astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         rho = np.where(a > 0, d / a, np.where(zero, 0.0, np.inf))
@@ -304,13 +338,15 @@ def _judge_chunk(c, g0, g1):
         cand = (a > 0) & (dl < 0.25)
         well = sigma <= 2.0 ** -20
         k_rel = float((np.abs(kg[well] - k_o[well]) / k_o[well]).max()) if well.any() else 0.0
+        # the oracle's code cell: y = MAX (|x| / amax)^k (rounded to FP32 before the encode, hence the
+        # 2^-24 added) must stay strictly between the grid midpoints around its code at both ends
         ci = np.flatnonzero(cand.ravel())
-        xs = x.ravel()[ci]
-        shrink = np.exp(-dl.ravel()[ci] / k_o[ci // G])
-        grow = np.exp(dl.ravel()[ci] / k_o[ci // G])
-    amo32, ko32 = am_o.astype(np.float32), k_o.astype(np.float32)
-    enc = lambda vals: orc.expand_encode_each(fmt, vals, amo32[ci // G], ko32[ci // G])
-    same = (enc(xs * shrink) == rc_[ci]) & (enc(xs * grow) == rc_[ci])
+        gi = ci // G
+        y = FMT_MAX[fmt] * (a.ravel()[ci] / am_o[gi]) ** k_o[gi]
+        lo_c, hi_c = cell_bounds(fmt)
+        mag = (rc_[ci] & 0x7F).astype(np.int64)
+        dli = dl.ravel()[ci] + 2.0 ** -24
+        same = (y * np.exp(-dli) > lo_c[mag]) & (y * np.exp(dli) < hi_c[mag])
     in_rule = zero.ravel().copy()
     in_rule[ci[same]] = True
     out = {"rule_n": int(in_rule.sum()), "rule_bad": 0, "rule_steps": 0, "want_bad": int(dw.size), "own_bad": 0,
