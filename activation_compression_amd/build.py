@@ -12,7 +12,6 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoat.so")
-CEILING_LIB = os.path.join(HERE, "libcoat_ceiling.so")  # memory-only reference kernels (benchmark only)
 ARCH = os.environ.get("COAT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -38,7 +37,6 @@ def _hipcc(out, srcs, verbose, extra=()):
 
 def build(verbose: bool = False, extra=()) -> str:
     _hipcc(LIB, sources(), verbose, extra)
-    _hipcc(CEILING_LIB, sorted(glob.glob(os.path.join(CSRC, "ceiling", "*.hip"))), verbose, extra)
     return LIB
 
 

@@ -5,15 +5,20 @@ HBM:
   1. the fused FP8-state AdamW step over the OLMo-7B-shaped parameter arena
      (6 888 095 744 FP32 master weights, BF16 gradients, m and v in E4M3,
      G = 128) -- one coat_adamw_step launch for the whole arena;
-  2. Group Scaling of a linear-layer input [16384 x 4096]: stage 1 + stage 2
-     (coat_group_absmax) and the per-tensor E4M3 cast (coat_quant_per_tensor);
-  3. 1x128 E4M3 group casts of the same tensor and of a SwiGLU input
-     [16384 x 11008] (coat_quant_group).
+  2. Group Scaling of a linear-layer input [16384 x 4096]: the 1x128 E4M3
+     group cast writes the per-slice maxima in the same pass (stage 1,
+     coat_quant_group), stage 2 reduces them (coat_absmax_reduce), and the
+     per-tensor E4M3 cast follows (coat_quant_per_tensor) -- two reads of X;
+  3. the 1x128 E4M3 group cast of a SwiGLU input [16384 x 11008].
 value = parameters updated per second of whole steps.  The roofline entry is
 the dominant kernel, the AdamW step: algorithmic bytes per launch
 (14 + 32/G bytes per parameter) over its average launch time, measured with
-HIP events on the stream it runs on.  The CPU baseline is the oracle on a
-bounded sample of the same step, on the host's cores.
+HIP events on the stream it runs on.  Each activation kernel is also timed
+alone after a read-only pass over 1 GiB has evicted the caches, so that its
+frac_of_peak is an HBM fraction (in the step the per-tensor cast re-reads X
+from the Infinity Cache).  The CPU baseline is the oracle on the host's
+cores: the 7B step on a contiguous 1/8 shard of the arena (extrapolated), and
+the other workloads in full.
 
 Beside the step (not in `value`), "extras" times the other entry points on
 the same resident workloads: the step with its BF16 working copy, the step as a
@@ -21,7 +26,7 @@ tensor-list launch (one entry per model tensor), the fused SwiGLU and RMSNorm
 producers with Group Scaling stage 1 in their epilogues,
 and the FP8 -> BF16 activation dequantization.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-baseline plan|quick|none] [--no-extras]
 """
 import argparse
 import hashlib
@@ -75,24 +80,44 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "_build", "libbench_ceiling.so")
+
+
+def ceiling_lib():
+    """The memory-only reference kernels (bench_ceiling.hip): built here with
+    hipcc for gfx950 when missing or older than the source."""
+    import ctypes
+    import subprocess
+
+    if not os.path.exists(CEILING_LIB) or os.path.getmtime(CEILING_LIB) < os.path.getmtime(CEILING_SRC):
+        os.makedirs(os.path.dirname(CEILING_LIB), exist_ok=True)
+        hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-o", CEILING_LIB + ".tmp", CEILING_SRC], check=True)
+        os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
+    L = ctypes.CDLL(CEILING_LIB)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.ceiling_step_skeleton.argtypes = [P] * 8 + [i64, i32, i32, P]
+    L.ceiling_copy_1r1w.argtypes = [P, P, i64, P]
+    L.ceiling_copy_4r3w.argtypes = [P] * 7 + [i64, P]
+    return L
+
+
 def memory_ceiling(theta, grad, st, n, alg_bytes, reps=3):
-    """What this device's HBM delivers for the step's own traffic: a memory-only
-    skeleton of the step (same bytes, same launch shape, lane layout and
-    residency cap, trivial arithmetic), the best of the skeleton over other
-    residency caps, and a plain one-read-one-write copy, all from
-    libcoat_ceiling.so.  Run after the timed region, on the benchmark's own
-    buffers (it overwrites them)."""
+    """What this device's HBM delivers for the step's own traffic, measured on
+    the benchmark's own buffers after the timed region (it overwrites them):
+    the memory-only skeleton of the step at residency caps of 2-5 workgroups
+    per CU (5 is the step's) and uncapped, with and without the per-group
+    metadata traffic; a plain one-read-one-write copy; and an equal-size copy
+    of four read and three write streams (the step's stream count)."""
     import ctypes
 
     import torch
 
-    path = os.path.join(ROOT, "activation_compression_amd", "libcoat_ceiling.so")
-    if not os.path.exists(path):
-        return None
-    L = ctypes.CDLL(path)
+    L = ceiling_lib()
     P = ctypes.c_void_p
-    L.coat_ceiling_step_skeleton.argtypes = [P] * 8 + [ctypes.c_int64, ctypes.c_int, P]
-    L.coat_ceiling_copy.argtypes = [P, P, ctypes.c_int64, P]
     stream = P(torch.cuda.current_stream().cuda_stream)
     ptrs = [P(t.data_ptr()) for t in (theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"],
                                       st["v_amax"], st["v_k"])]
@@ -108,17 +133,29 @@ def memory_ceiling(theta, grad, st, n, alg_bytes, reps=3):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms_skel = timed(lambda: L.coat_ceiling_step_skeleton(*ptrs, n, 5, stream))
-    best = {}
-    for b in (2, 3, 4, 6, 0):
-        best[b] = timed(lambda: L.coat_ceiling_step_skeleton(*ptrs, n, b, stream))
-    b_best = min(best, key=best.get)
-    nbytes = grad.numel() * grad.element_size()
-    ms_copy = timed(lambda: L.coat_ceiling_copy(P(theta.data_ptr()), P(grad.data_ptr()), nbytes, stream))
-    return {"step_memory_skeleton_gb_per_s": round(alg_bytes / (ms_skel * 1e-3) / 1e9, 1),
-            "best_memory_skeleton_gb_per_s": round(alg_bytes / (min(best[b_best], ms_skel) * 1e-3) / 1e9, 1),
-            "best_memory_skeleton_blocks_per_cu": b_best if best[b_best] < ms_skel else 5,
-            "copy_gb_per_s": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1)}
+    gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+    alg_nometa = n * 14.0
+    skel, nometa = {}, {}
+    for cap in (2, 3, 4, 5, 0):
+        skel[cap] = timed(lambda: L.ceiling_step_skeleton(*ptrs, n, cap, 1, stream))
+        nometa[cap] = timed(lambda: L.ceiling_step_skeleton(*ptrs, n, cap, 0, stream))
+    b_best = min(skel, key=skel.get)
+    nb = grad.numel() * grad.element_size()
+    ms_copy = timed(lambda: L.ceiling_copy_1r1w(P(theta.data_ptr()), P(grad.data_ptr()), nb, stream))
+    S = theta.numel() * 4 // 7 // 16 * 16
+    base = theta.data_ptr()
+    streams = [P(base + i * S) for i in range(7)]
+    ms_4r3w = timed(lambda: L.ceiling_copy_4r3w(*streams, S, stream))
+    name = lambda c: f"cap{c}" if c else "uncapped"
+    return {"step_memory_skeleton_gb_per_s": gbs(alg_bytes, skel[5]),
+            "best_memory_skeleton_gb_per_s": gbs(alg_bytes, skel[b_best]),
+            "best_memory_skeleton_blocks_per_cu": b_best or "uncapped",
+            "skeleton_gb_per_s_by_residency": {name(c): gbs(alg_bytes, skel[c]) for c in skel},
+            "skeleton_without_metadata_gb_per_s_by_residency": {name(c): gbs(alg_nometa, nometa[c]) for c in nometa},
+            "copy_gb_per_s": gbs(2 * nb, ms_copy),
+            "copy_4r3w_equal_streams_gb_per_s": gbs(7 * S, ms_4r3w),
+            "note": ("skeleton times: the step's bytes with trivial arithmetic; without metadata it moves 14 B per "
+                     "parameter and its GB/s counts those")}
 
 
 def state_diagnostics(st, sample=1 << 22):
@@ -168,6 +205,61 @@ def entry(alg_bytes, ms, elems=None):
     if elems:
         d["elements_per_s"] = elems / (ms * 1e-3)
     return d
+
+
+def cold_activation_times(coat, xs, partial, amax, codes_pt, scale_pt, gcodes, gscales, G, reps=10):
+    """Each activation kernel of the step alone, after a read-only pass over
+    1 GiB has evicted the L2s and the 256 MB Infinity Cache: average of `reps`
+    launches, HIP events around the kernel only.  Also both stages of Group
+    Scaling as one standalone call (coat_group_absmax), cold and warm (right
+    after a launch over the same input)."""
+    import torch
+
+    evict = torch.ones(1 << 28, device="cuda")   # 1 GiB
+
+    def cold(fn):
+        tot = 0.0
+        for _ in range(reps):
+            evict.amax()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / reps
+
+    def warm(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {
+        "quant_group_stage1_linear": cold(lambda: coat.coat_quant_group(xs[0], gcodes[0], gscales[0], partial,
+                                                                        group_size=G)),
+        "absmax_reduce": cold(lambda: coat.coat_absmax_reduce(partial, amax)),
+        "quant_per_tensor": cold(lambda: coat.coat_quant_per_tensor(xs[0], amax, codes_pt, scale_pt)),
+        "quant_group_swiglu": cold(lambda: coat.coat_quant_group(xs[1], gcodes[1], gscales[1], None,
+                                                                 group_size=G)),
+    }
+    N0 = xs[0].numel()
+    ga = lambda: coat.coat_group_absmax(xs[0], partial, amax, group_size=G)
+    b = N0 * 2 + 2 * 4 * N0 / G
+    c_ms, w_ms = cold(ga), warm(ga)
+    out["group_absmax_standalone"] = {
+        "cold": entry(b, c_ms, N0), "warm_cache_assisted": entry(b, w_ms, N0),
+        "note": ("both stages of Group Scaling as one call, outside the step (whose stage 1 comes from the "
+                 "1x128 cast's pass); warm: right after a launch over the same input, which the Infinity "
+                 "Cache then holds")}
+    del evict
+    torch.cuda.synchronize()
+    return out
 
 
 def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
@@ -292,67 +384,118 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     return out
 
 
-def cpu_baseline(spec, acts, G, threads):
-    """The oracle (as it stands) on a bounded sample of one step, scaled to
-    params/s of the whole step.  Sample: the first two tensors of the arena
-    (l0.qkv, l0.out: 67 108 864 parameters) for the AdamW step -- timed on
-    step 2 so that the moments it dequantizes are nonzero -- and the first
-    2048 rows of each activation tensor for Group Scaling and the casts."""
+def _oracle_steps(spec, threads, steps=(1, 2), time_steps=(2,), tensors=None):
+    """Run the oracle's step on (a prefix of the tensors of) an arena from a
+    fresh state; returns (parameters, seconds of each step in time_steps)."""
     import numpy as np
 
     import oracle as orc
     from activation_compression_amd import inputs
 
-    n_tensors = 2
-    sub = inputs.ArenaSpec(spec.name + "-sample", spec.config, spec.tensors[:n_tensors], spec.v_fmt, G,
-                           spec.grad_scale)
-    n = sub.numel
+    sub = spec if tensors is None else inputs.ArenaSpec(spec.name + "-shard", spec.config, spec.tensors[:tensors],
+                                                        spec.v_fmt, spec.group_size, spec.grad_scale)
+    n, G = sub.numel, sub.group_size
     theta = inputs.gen_params(sub).numpy()
     st = {k: v.numpy() for k, v in inputs.fresh_state(n, G).items()}
     f32 = lambda v: float(np.float32(v))
-    hp = lambda t: orc.hparams(f32(inputs.LR), f32(inputs.BETA1), f32(inputs.BETA2), f32(inputs.EPS),
-                               f32(inputs.WEIGHT_DECAY), t)
-    g1 = inputs.gen_grads(sub, 1).numpy().view(np.uint16)
-    g2 = inputs.gen_grads(sub, 2).numpy().view(np.uint16)
-    args = lambda: (theta, None, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"], st["v_k"])
-    a = list(args()); a[1] = g1
-    orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(1), threads=threads)
-    m1 = 8 << 20  # the single-thread sample: the first 8 Mi parameters, same step 2
-    th1 = theta[:m1].copy()
-    st1 = {k: (v[:m1].copy() if k.endswith("codes") else v[:m1 // G].copy()) for k, v in st.items()}
-    a = list(args()); a[1] = g2
-    t0 = time.perf_counter()
-    orc.adamw_step(*a, G=G, v_fmt=spec.v_fmt, hp=hp(2), threads=threads)
-    t_step = (time.perf_counter() - t0) * spec.numel / n
+    secs = []
+    for t in steps:
+        g = inputs.gen_grads(sub, t).numpy().view(np.uint16)
+        hp = orc.hparams(f32(inputs.LR), f32(inputs.BETA1), f32(inputs.BETA2), f32(inputs.EPS),
+                         f32(inputs.WEIGHT_DECAY), t)
+        t0 = time.perf_counter()
+        orc.adamw_step(theta, g, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"], st["v_k"],
+                       G=G, v_fmt=sub.v_fmt, hp=hp, threads=threads)
+        if t in time_steps:
+            secs.append(time.perf_counter() - t0)
+    return n, secs
 
-    t_act = 0.0
-    rows = 2048
+
+def _oracle_activations(acts, G, threads, rows=None):
+    """The step's activation pass on the oracle: stage 1 and stage 2 and the
+    per-tensor cast of the first tensor, the 1xG cast of both (on the first
+    `rows` rows of each when given, scaled to the whole tensors)."""
+    import numpy as np
+
+    import oracle as orc
+    from activation_compression_amd import inputs
+
+    tot = 0.0
     for i, act in enumerate(acts):
-        x = inputs.gen_activation(inputs.ActivationSpec(act.name, rows, act.cols, act.seed)).numpy().view(np.uint16)
+        r = act.rows if rows is None else rows
+        x = inputs.gen_activation(inputs.ActivationSpec(act.name, r, act.cols, act.seed)).numpy().view(np.uint16)
         t0 = time.perf_counter()
         if i == 0:
             _, amax = orc.group_absmax(x, G, threads=threads)
             orc.quant_per_tensor(x, amax, threads=threads)
         orc.quant_group(x, G, threads=threads)
-        t_act += (time.perf_counter() - t0) * act.rows / rows
-    total = t_step + t_act
+        tot += (time.perf_counter() - t0) * act.rows / r
+    return tot
 
-    t0 = time.perf_counter()
-    orc.adamw_step(th1, g2[:m1], st1["m_codes"], st1["m_amax"], st1["m_k"], st1["v_codes"], st1["v_amax"],
-                   st1["v_k"], G=G, v_fmt=spec.v_fmt, hp=hp(2), threads=1)
-    single = m1 / (time.perf_counter() - t0)
-    return {
-        "value": spec.numel / total,
+
+def cpu_baseline(spec, acts, G, threads, plan=True):
+    """The binary64 C oracle (as it stands) on the host's cores.
+
+    value: params/s of the benchmark's whole step -- the OLMo-7B-shaped AdamW
+    step timed on a contiguous 1/8 shard of the arena (its first tensors, the
+    largest prefix within n/8; step 2 from the oracle's own step 1, so that the
+    dequantized moments are nonzero) and extrapolated linearly to the whole
+    arena, plus the activation pass on the full tensors.  plan=True also times
+    the other workloads in full: the single 1024x1024 tensor (ten steps), the
+    OLMo-1B-shaped set (step 2), the 64 Mi stress set for G in {32, 128, 512}
+    x both v formats (its step 1 and step 2), and a single-thread rate."""
+    import numpy as np  # noqa: F401
+
+    from activation_compression_amd import inputs
+
+    sizes = [r * c for _, (r, c) in spec.tensors]
+    k, acc = 0, 0
+    while k < len(sizes) and acc + sizes[k] <= spec.numel // 8:
+        acc += sizes[k]
+        k += 1
+    n_shard, (t_shard,) = _oracle_steps(spec, threads, tensors=k)
+    t_step = t_shard * spec.numel / n_shard
+    if plan:
+        t_act = _oracle_activations(acts, G, threads)
+        act_note = "the activation pass on the full tensors"
+    else:
+        t_act = _oracle_activations(acts, G, threads, rows=2048)
+        act_note = "the activation pass on the first 2048 rows of each tensor (scaled)"
+    out = {
+        "value": spec.numel / (t_step + t_act),
         "unit": "params/s",
         "cores": threads,
         "kind": "oracle",
-        "single_thread_step_params_per_s": single,
-        "sample": (f"AdamW step 2 on the first {n_tensors} tensors of the arena ({n} params, scaled x"
-                   f"{spec.numel / n:.1f}); Group Scaling + casts on the first {rows} rows of each "
-                   f"activation tensor (scaled); binary64 C oracle, {threads} threads; the single-thread "
-                   f"rate is the same step on the first {m1} params"),
-        "seconds_per_step": total,
+        "sample": (f"OLMo-7B-shaped AdamW step 2 on a contiguous shard of the arena (its first {k} tensors, "
+                   f"{n_shard} params = 1/{spec.numel / n_shard:.3f} of it), extrapolated x"
+                   f"{spec.numel / n_shard:.3f}; {act_note}; binary64 C oracle, {threads} threads"),
+        "extrapolated": True,
+        "seconds_per_step": t_step + t_act,
+        "step_params_per_s": spec.numel / t_step,
+        "activation_pass_s": t_act,
     }
+    if plan:
+        cfg = {}
+        s1 = inputs.single_1024()
+        n1, secs = _oracle_steps(s1, threads, steps=range(1, 11), time_steps=range(1, 11))
+        cfg["single_1024x1024_10_steps"] = {"params": n1, "s_per_step": sum(secs) / 10,
+                                            "params_per_s": n1 * 10 / sum(secs)}
+        s3 = inputs.olmo_1b()
+        n3, (t3,) = _oracle_steps(s3, threads)
+        cfg["olmo_1b_shaped_step2"] = {"params": n3, "s_per_step": t3, "params_per_s": n3 / t3}
+        for g_ in (32, 128, 512):
+            for f_ in ("e4m3", "e5m2"):
+                s5 = inputs.stress(g_, f_)
+                n5, (a5, b5) = _oracle_steps(s5, threads, time_steps=(1, 2))
+                cfg[f"stress_64Mi_G{g_}_{f_}"] = {"params": n5, "s_step1": a5, "s_step2": b5,
+                                                   "params_per_s_step1": n5 / a5}
+        cfg["activations_full"] = {"s": t_act, "tensors": [[a.rows, a.cols] for a in acts]}
+        m1 = 8 << 20
+        s1t = inputs.ArenaSpec("single-thread-8Mi", 4, (("w", (m1 // 4096, 4096)),), spec.v_fmt, G, "tensor")
+        n1t, (tt,) = _oracle_steps(s1t, 1)
+        out["single_thread_step_params_per_s"] = n1t / tt
+        out["configs"] = cfg
+    return out
 
 
 def main():
@@ -361,6 +504,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline", choices=("plan", "quick", "none"), default="plan",
+                    help="plan: the 7B step on a 1/8 shard plus every other workload in full; quick: the shard "
+                         "and a sample of the activations only")
     ap.add_argument("--no-extras", action="store_true", help="skip the entry points timed beside the step")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -416,11 +562,11 @@ def main():
         coat.coat_adamw_step(theta, grad, st["m_codes"], st["m_amax"], st["m_k"], st["v_codes"], st["v_amax"],
                              st["v_k"], group_size=G, v_format=spec.v_fmt, hp=hp)
         if marks: marks[1].record()
-        coat.coat_group_absmax(xs[0], partial, amax, group_size=G)
+        coat.coat_quant_group(xs[0], gcodes[0], gscales[0], partial, group_size=G)
         if marks: marks[2].record()
-        coat.coat_quant_per_tensor(xs[0], amax, codes_pt, scale_pt)
+        coat.coat_absmax_reduce(partial, amax)
         if marks: marks[3].record()
-        coat.coat_quant_group(xs[0], gcodes[0], gscales[0], None, group_size=G)
+        coat.coat_quant_per_tensor(xs[0], amax, codes_pt, scale_pt)
         if marks: marks[4].record()
         coat.coat_quant_group(xs[1], gcodes[1], gscales[1], None, group_size=G)
         if marks: marks[5].record()
@@ -443,21 +589,31 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
 
-    names = ["adamw_fp8_step", "group_absmax", "quant_per_tensor", "quant_group_linear", "quant_group_swiglu"]
+    names = ["adamw_fp8_step", "quant_group_stage1_linear", "absmax_reduce", "quant_per_tensor",
+             "quant_group_swiglu"]
     per = {nm: sum(m[j].elapsed_time(m[j + 1]) for m in marks) / args.steps for j, nm in enumerate(names)}
     bpp = step_bytes_per_param(G)
+    N0, N1 = acts[0].numel, acts[1].numel
     alg = {
         "adamw_fp8_step": n * bpp,
-        "group_absmax": acts[0].numel * 2 + 2 * 4 * acts[0].numel / G,
-        "quant_per_tensor": acts[0].numel * 3,
-        "quant_group_linear": acts[0].numel * 3 + 4 * acts[0].numel / G,
-        "quant_group_swiglu": acts[1].numel * 3 + 4 * acts[1].numel / G,
+        "quant_group_stage1_linear": N0 * 3 + 8 * N0 / G,   # codes, scales and stage-1 partials
+        "absmax_reduce": 4 * N0 / G + 4,
+        "quant_per_tensor": N0 * 3,
+        "quant_group_swiglu": N1 * 3 + 4 * N1 / G,
     }
-    elems = {"adamw_fp8_step": n, "group_absmax": acts[0].numel, "quant_per_tensor": acts[0].numel,
-             "quant_group_linear": acts[0].numel, "quant_group_swiglu": acts[1].numel}
-    kernels = {nm: entry(alg[nm], per[nm], elems[nm]) for nm in names}
-    kernels["group_absmax"]["note"] = ("runs right after the optimizer step and shares HBM with the write-back "
-                                       "of the step's last dirty cache lines")
+    elems = {"adamw_fp8_step": n, "quant_group_stage1_linear": N0, "absmax_reduce": N0 // G,
+             "quant_per_tensor": N0, "quant_group_swiglu": N1}
+    # activation kernels: frac_of_peak from launches after a cache eviction (HBM fractions); the
+    # in-step times beside them
+    cold = cold_activation_times(coat, xs, partial, amax, codes_pt, scale_pt, gcodes, gscales, G)
+    kernels = {"adamw_fp8_step": entry(alg["adamw_fp8_step"], per["adamw_fp8_step"], n)}
+    for nm in names[1:]:
+        kernels[nm] = entry(alg[nm], cold[nm], elems[nm])
+        kernels[nm]["cache"] = "cold: after a read-only pass over 1 GiB"
+        kernels[nm]["in_step_ms"] = round(per[nm], 4)
+    kernels["quant_per_tensor"]["in_step_note"] = (
+        "in the step X was read by the 1x128 cast just before and is served from the Infinity Cache")
+    kernels["group_absmax_standalone"] = cold["group_absmax_standalone"]
     step_ms = sorted(m[0].elapsed_time(m[5]) for m in marks)
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * sum(step_ms[len(step_ms) // 2 - 1:][:2])
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
@@ -470,10 +626,11 @@ def main():
         ceiling["frac_of_best_memory_skeleton"] = round(achieved / ceiling["best_memory_skeleton_gb_per_s"], 4)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.cpu_baseline != "none":
         threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
-        log(f"timing the oracle on a bounded sample with {threads} threads")
-        cpu = cpu_baseline(spec, acts, G, threads)
+        log(f"timing the oracle ({args.cpu_baseline}) with {threads} threads")
+        del theta, grad, st
+        cpu = cpu_baseline(spec, acts, G, threads, plan=args.cpu_baseline == "plan")
 
     out = {
         "metric": "FP8-state AdamW params updated/s + achieved HBM GB/s (% of peak), 1xMI355X",
