@@ -73,6 +73,8 @@ def lib():
     L.coat_adamw_list_pack.restype = ctypes.c_int
     L.coat_adamw_step_list.argtypes = [P, P, ctypes.c_int, ctypes.POINTER(AdamWHParams), P]
     L.coat_adamw_step_list.restype = ctypes.c_int
+    L.coat_adamw_step_list_noalloc.argtypes = [P, ctypes.c_int, ctypes.POINTER(AdamWHParams), P]
+    L.coat_adamw_step_list_noalloc.restype = ctypes.c_int
     L.coat_status_string.argtypes = [ctypes.c_int]
     L.coat_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -237,7 +239,7 @@ class AdamWTensorList:
     param_bf16 (device tensors, one allocation each is fine).  Build it once;
     it stays valid while those tensors live, and keeps references to them."""
 
-    def __init__(self, states, *, group_size: int = 128):
+    def __init__(self, states, *, group_size: int = 128, device_copy: bool = True):
         n_t = len(states)
         arr = (AdamWTensor * max(n_t, 1))()
         for i, s in enumerate(states):
@@ -257,7 +259,8 @@ class AdamWTensorList:
         self.host = np.zeros(nbytes, dtype=np.uint8)
         _check(lib().coat_adamw_list_pack(arr, n_t, group_size, ctypes.c_void_p(self.host.ctypes.data)),
                "coat_adamw_list_pack")
-        self.device = torch.from_numpy(self.host).to("cuda")
+        # device_copy=False: for coat_adamw_step_list_noalloc only, which copies the table itself
+        self.device = torch.from_numpy(self.host).to("cuda") if device_copy else None
         self.group_size = group_size
         self._refs = list(states)
 
@@ -266,3 +269,11 @@ def coat_adamw_step_list(tlist: AdamWTensorList, *, v_format="e4m3", hp: AdamWHP
     """One fused FP8-state AdamW step over every tensor of the list, one launch."""
     _check(lib().coat_adamw_step_list(ctypes.c_void_p(tlist.host.ctypes.data), _ptr(tlist.device, _U8, "table"),
                                       _FMT[v_format], ctypes.byref(hp), _stream(stream)), "coat_adamw_step_list")
+
+
+def coat_adamw_step_list_noalloc(tlist: AdamWTensorList, *, v_format="e4m3", hp: AdamWHParams, stream=None) -> None:
+    """coat_adamw_step_list with the table in the library's own device array
+    (no device memory is allocated by the call).  The host table stays alive
+    with `tlist`, which the caller keeps until the stream has run the call."""
+    _check(lib().coat_adamw_step_list_noalloc(ctypes.c_void_p(tlist.host.ctypes.data), _FMT[v_format],
+                                              ctypes.byref(hp), _stream(stream)), "coat_adamw_step_list_noalloc")

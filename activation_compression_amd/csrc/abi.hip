@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/coat.h"
 #include "kernels.hpp"
@@ -75,6 +76,7 @@ const char *coat_status_string(coat_status s) {
     case COAT_ERR_FORMAT: return "unknown FP8 format";
     case COAT_ERR_HPARAM: return "invalid AdamW hyper-parameters";
     case COAT_ERR_HIP: return "HIP runtime error while enqueueing";
+    case COAT_ERR_SCRATCH: return "the request exceeds the library's static device scratch";
     }
     return "unknown status";
 }
@@ -329,6 +331,73 @@ coat_status coat_adamw_step_list(const void *table_host, const void *table_devic
     if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
     if (!valid_hparams(hp)) return COAT_ERR_HPARAM;
     const unsigned char *dev = static_cast<const unsigned char *>(table_device);
+    coat::StepListArgs a;
+    a.chunk_start = reinterpret_cast<const int64_t *>(dev + sizeof(ListHeader));
+    a.entries = reinterpret_cast<const coat::StepBufs *>(dev + sizeof(ListHeader) + list_starts_bytes(h.n_tensors));
+    a.total_chunks = h.total_chunks;
+    a.n_tensors = h.n_tensors;
+    a.has_bf16 = h.has_bf16;
+    make_params(hp, v_format, a.p);
+    return from_hip(coat::launch_adamw_fp8_step_list(a, h.group_size, (int)v_format, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---- the tensor-list step without allocation ------------------------------
+//
+// coat_adamw_step_list reads its packed table from device memory the caller
+// owns.  The variant below keeps that table in `scratch`, a file-scope device
+// array that every GPU the library runs on holds until the process ends; the
+// call copies the host table into it on the caller's stream and launches the
+// same kernel on it, so it allocates nothing.  Host code never passes the
+// array's name itself (on the host that is only a stand-in for the symbol):
+// its address on each device comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[COAT_LIST_NOALLOC_MAX_BYTES];
+
+// The current device's address of `scratch` (nullptr if it cannot be had).
+void *scratch_on_current_device() {
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex lock;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> g(lock);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        addr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+coat_status coat_adamw_step_list_noalloc(const void *table_host, coat_fp8_format v_format,
+                                         const coat_adamw_hparams *hp, void *stream) {
+    if (!table_host || !hp) return COAT_ERR_NULL;
+    ListHeader h;
+    memcpy(&h, table_host, sizeof h);
+    if (h.magic != kListMagic || h.version != kListVersion || h.n_tensors <= 0 || h.total_chunks <= 0)
+        return COAT_ERR_SHAPE;
+    if (!valid_group(h.group_size)) return COAT_ERR_GROUP;
+    if (v_format != COAT_FP8_E4M3 && v_format != COAT_FP8_E5M2) return COAT_ERR_FORMAT;
+    if (!valid_hparams(hp)) return COAT_ERR_HPARAM;
+    const int64_t bytes = coat_adamw_list_bytes(h.n_tensors);
+    if (bytes <= 0 || bytes > (int64_t)COAT_LIST_NOALLOC_MAX_BYTES) return COAT_ERR_SCRATCH;
+    unsigned char *dev = static_cast<unsigned char *>(scratch_on_current_device());
+    if (!dev) return COAT_ERR_HIP;
+    if (hipMemcpyAsync(dev, table_host, (size_t)bytes, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
+        return COAT_ERR_HIP;
     coat::StepListArgs a;
     a.chunk_start = reinterpret_cast<const int64_t *>(dev + sizeof(ListHeader));
     a.entries = reinterpret_cast<const coat::StepBufs *>(dev + sizeof(ListHeader) + list_starts_bytes(h.n_tensors));

@@ -57,7 +57,9 @@ typedef enum {
                             step < 1, non-finite lr / wd / eps, or
                             lr / (1 - beta1^step) or 1 - lr * wd not finite
                             in FP32                                             */
-    COAT_ERR_HIP = 7     /* the HIP runtime refused the launch                  */
+    COAT_ERR_HIP = 7,    /* the HIP runtime refused the launch                  */
+    COAT_ERR_SCRATCH = 8 /* the request exceeds the library's static device
+                            scratch (coat_adamw_step_list_noalloc only)        */
 } coat_status;
 
 typedef enum {
@@ -180,6 +182,31 @@ coat_status coat_adamw_list_pack(const coat_adamw_tensor *tensors, int32_t n_ten
  * the packer's header -> COAT_ERR_SHAPE. */
 coat_status coat_adamw_step_list(const void *table_host, const void *table_device, coat_fp8_format v_format,
                                  const coat_adamw_hparams *hp, void *stream);
+
+/*
+ * coat_adamw_step_list_noalloc -- coat_adamw_step_list for callers that cannot
+ * allocate device memory: code that must not call hipMalloc (tight training
+ * or serving loops, harnesses that forbid allocation) and so has no device
+ * copy of the table to pass.  The table is copied, on `stream`, into a device
+ * array the library owns -- COAT_LIST_NOALLOC_MAX_BYTES (64 KiB, enough for
+ * 744 tensors; coat_adamw_list_bytes gives a table's size), held by every GPU
+ * the library runs on until the process ends -- and the same kernel then
+ * reads it there.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.
+ *
+ * table_host  the table coat_adamw_list_pack wrote.  It is read by the copy
+ *             the call enqueues: keep it unchanged until `stream` has run
+ *             that copy (as for any asynchronous copy from host memory).
+ * v_format, hp, stream  as coat_adamw_step_list; the result is identical.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (other streams, other host threads) race, and must be ordered by
+ * the caller.  A table larger than COAT_LIST_NOALLOC_MAX_BYTES ->
+ * COAT_ERR_SCRATCH; other errors as coat_adamw_step_list; nothing is enqueued
+ * on error.
+ */
+#define COAT_LIST_NOALLOC_MAX_BYTES 65536
+coat_status coat_adamw_step_list_noalloc(const void *table_host, coat_fp8_format v_format,
+                                         const coat_adamw_hparams *hp, void *stream);
 
 /*
  * coat_group_absmax -- both stages of Group Scaling ([COAT] section "mixed
