@@ -26,17 +26,19 @@ __device__ __forceinline__ void dequant16(const uint32_t c[4], float scale, uint
     }
 }
 
+// A wave issues its code loads before it reads the scale, so the scalar's
+// latency overlaps the loads'.
 __global__ __launch_bounds__(kBlock) void dequant_per_tensor_kernel(const uint8_t *__restrict__ codes, int64_t n,
                                                                     int64_t n_chunks,
                                                                     const float *__restrict__ scale_p,
                                                                     uint16_t *__restrict__ out) {
-    const float scale = *scale_p;
     const int lane = threadIdx.x & 63;
     const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= n_chunks) return;
     const int64_t e0 = chunk * kWaveElems + lane * 16;
     if (e0 + 16 <= n) {
         const uint4 cv = *reinterpret_cast<const uint4 *>(codes + e0);
+        const float scale = *scale_p;
         const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
         uint32_t o[8];
         dequant16(c, scale, o);
@@ -45,6 +47,7 @@ __global__ __launch_bounds__(kBlock) void dequant_per_tensor_kernel(const uint8_
         op[1] = make_uint4(o[4], o[5], o[6], o[7]);
     } else if (e0 < n) {  // n % 16 == 8: the last lane holds 8 codes
         const uint2 cv = *reinterpret_cast<const uint2 *>(codes + e0);
+        const float scale = *scale_p;
         const uint32_t c[4] = {cv.x, cv.y, 0u, 0u};
         uint32_t o[8];
         dequant16(c, scale, o);

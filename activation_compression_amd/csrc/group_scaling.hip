@@ -81,31 +81,34 @@ __global__ __launch_bounds__(kBlock) void absmax_stage2_kernel(const float *__re
 
 __global__ void zero_scalar_kernel(float *p) { *p = 0.0f; }
 
-// ---- per-tensor cast with the device-resident tensor absmax.
+// ---- per-tensor cast with the device-resident tensor absmax.  A wave issues
+// its input loads before it reads the absmax (which the stage-2 kernel before
+// it has just written), so the scalar's latency overlaps the loads'.
 __global__ __launch_bounds__(kBlock) void quant_per_tensor_kernel(const uint16_t *__restrict__ x, int64_t n,
                                                                   int64_t n_chunks, const float *__restrict__ amax,
                                                                   uint8_t *__restrict__ codes,
                                                                   float *__restrict__ scale) {
-    const float A = *amax;
-    const CastQ q = cast_q(A);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = A > 0.0f ? A / 448.0f : 1.0f;
     const int lane = threadIdx.x & 63;
     const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) + (threadIdx.x >> 6);  // one chunk per wave
-    if (chunk < n_chunks) {
-        const int64_t e0 = chunk * kWaveElems + lane * 16;
-        if (e0 + 16 <= n) {
-            uint32_t w[8];
-            load16(x + e0, w);
-            *reinterpret_cast<uint4 *>(codes + e0) = cast16<true>(w, q);
-        } else if (e0 < n) {  // n % 16 == 8: the last lane holds 8 values
-            uint32_t w[8];
-            const uint4 a = reinterpret_cast<const uint4 *>(x + e0)[0];
-            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-            w[4] = w[5] = w[6] = w[7] = 0u;
-            const uint4 c = cast16<true>(w, q);
-            *reinterpret_cast<uint2 *>(codes + e0) = make_uint2(c.x, c.y);
-        }
+    const int64_t e0 = chunk * kWaveElems + lane * 16;
+    const bool live = chunk < n_chunks;
+    const bool full = live && e0 + 16 <= n;
+    const bool tail = live && !full && e0 < n;  // n % 16 == 8: the last lane holds 8 values
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (full) {
+        load16(x + e0, w);
+    } else if (tail) {
+        const uint4 a = reinterpret_cast<const uint4 *>(x + e0)[0];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     }
+    const float A = *amax;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = A > 0.0f ? A / 448.0f : 1.0f;
+    if (!(full || tail)) return;
+    const uint4 c = cast16<true>(w, cast_q(A));
+    if (full)
+        *reinterpret_cast<uint4 *>(codes + e0) = c;
+    else
+        *reinterpret_cast<uint2 *>(codes + e0) = make_uint2(c.x, c.y);
 }
 
 // ---- 1xG group cast (+ optional stage-1 partials from the same pass).
