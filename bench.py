@@ -84,20 +84,27 @@ CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "_build", "libbench_ceiling.so")
 
 
-def ceiling_lib():
-    """The memory-only reference kernels (bench_ceiling.hip): built here with
-    hipcc for gfx950 when missing or older than the source."""
-    import ctypes
+def build_ceiling_lib(force=False):
+    """Compile the memory-only reference kernels (bench_ceiling.hip) with hipcc
+    for gfx950 into _build/, when forced or when the library is missing or
+    older than the source."""
     import subprocess
 
-    if not os.path.exists(CEILING_LIB) or os.path.getmtime(CEILING_LIB) < os.path.getmtime(CEILING_SRC):
+    if force or not os.path.exists(CEILING_LIB) or os.path.getmtime(CEILING_LIB) < os.path.getmtime(CEILING_SRC):
         os.makedirs(os.path.dirname(CEILING_LIB), exist_ok=True)
         hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
         subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                         "-o", CEILING_LIB + ".tmp", CEILING_SRC], check=True)
         os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
-    L = ctypes.CDLL(CEILING_LIB)
+    return CEILING_LIB
+
+
+def ceiling_lib():
+    """The memory-only reference kernels, built first if needed."""
+    import ctypes
+
+    L = ctypes.CDLL(build_ceiling_lib())
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.ceiling_step_skeleton.argtypes = [P] * 8 + [i64, i32, i32, P]
     L.ceiling_copy_1r1w.argtypes = [P, P, i64, P]
@@ -297,6 +304,7 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     out[f"adamw_fp8_step_list_{len(views)}_tensors"] = entry(n * (14.0 + 32.0 / G), ms, n)
     del tl, views
 
+    log("extras: the stress set and the single 1024 x 1024 tensor")
     # the stress set (64 Mi params, gradients over ten decades, 5% zeros) for
     # G in {32, 128, 512} and both v formats, and the single 1024 x 1024 tensor
     # (a launch-bound correctness workload): average of 10 steps after 2
@@ -311,6 +319,7 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
         out[f"adamw_fp8_step_{sp.name}"] = entry(ns * (14.0 + 32.0 / sp.group_size), ms_s, ns)
         del ths, gs_, sts
 
+    log("extras: the OLMo-1B-shaped set")
     # the OLMo-1B-shaped parameter set (v in E5M2): five steps from a fresh
     # state, the median of steps 2-5 (each step timed alone)
     s1 = inputs.olmo_1b()
@@ -331,6 +340,7 @@ def extras(coat, inputs, theta, grad, st, spec, G, step0, reps=10):
     out["adamw_fp8_step_olmo1b_e5m2"] = entry(n1 * (14.0 + 32.0 / G), sum(ms1) / 2, n1)
     del th1, g1, st1
 
+    log("extras: the fused producers and the dequantizations")
     gs, us = inputs.swiglu_gate(), inputs.swiglu_up()
     N = gs.numel
     gate, up = inputs.gen_activation(gs, device="cuda"), inputs.gen_activation(us, device="cuda")
@@ -576,6 +586,7 @@ def main():
         step += 1
         one_step(step)
     torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
     marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -588,6 +599,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
+    log(f"timed region done: {ms_per_step:.3f} ms per step")
 
     names = ["adamw_fp8_step", "quant_group_stage1_linear", "absmax_reduce", "quant_per_tensor",
              "quant_group_swiglu"]
@@ -605,6 +617,7 @@ def main():
              "quant_per_tensor": N0, "quant_group_swiglu": N1}
     # activation kernels: frac_of_peak from launches after a cache eviction (HBM fractions); the
     # in-step times beside them
+    log("activation kernels from a cold cache")
     cold = cold_activation_times(coat, xs, partial, amax, codes_pt, scale_pt, gcodes, gscales, G)
     kernels = {"adamw_fp8_step": entry(alg["adamw_fp8_step"], per["adamw_fp8_step"], n)}
     for nm in names[1:]:
@@ -619,7 +632,10 @@ def main():
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
     traffic = measured_traffic()
     diag = state_diagnostics(st)
+    if not args.no_extras:
+        log("extras: the other entry points and workloads")
     extra = None if args.no_extras else extras(coat, inputs, theta, grad, st, spec, G, step + 1)
+    log("memory ceiling of the step's traffic")
     ceiling = memory_ceiling(theta, grad, st, n, alg["adamw_fp8_step"])
     if ceiling:
         ceiling["frac_of_step_memory_skeleton"] = round(achieved / ceiling["step_memory_skeleton_gb_per_s"], 4)
