@@ -26,8 +26,9 @@ template <> struct Fp8<kE5M2> {
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 // ---- native FP8 conversions (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 and the
-// reverse).  Rounding is to nearest even; callers clamp to +-MAX first, which
-// makes the result the saturating rounding whatever the overflow mode.
+// reverse).  Rounding is to nearest even.  Callers pass values within a few
+// ulps of +-MAX or below (clamped, or bounded by construction), which the
+// rounding takes to at most MAX whatever the overflow mode.
 
 // Pack four FP32 values into four FP8 codes (byte i <- value i).
 template <int F>
