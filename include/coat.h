@@ -201,8 +201,9 @@ coat_status coat_adamw_step_list(const void *table_host, const void *table_devic
  * Every call on one GPU shares that GPU's array: calls that may overlap on
  * one GPU (other streams, other host threads) race, and must be ordered by
  * the caller.  A table larger than COAT_LIST_NOALLOC_MAX_BYTES ->
- * COAT_ERR_SCRATCH; other errors as coat_adamw_step_list; nothing is enqueued
- * on error.
+ * COAT_ERR_SCRATCH; other errors as coat_adamw_step_list.  A call rejected by
+ * its argument checks enqueues nothing; if the launch itself fails
+ * (COAT_ERR_HIP), the table copy may already be enqueued.
  */
 #define COAT_LIST_NOALLOC_MAX_BYTES 65536
 coat_status coat_adamw_step_list_noalloc(const void *table_host, coat_fp8_format v_format,
