@@ -421,7 +421,7 @@ template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_kernel(const StepArgs a) {
     __shared__ float2 tab[512];
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
+    const int64_t chunk = xcd_eighth(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const bool live = chunk < a.n_chunks;
     const int64_t base = live ? chunk * kWaveElems : 0;
@@ -446,7 +446,7 @@ template <int G, int VF, bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw_fp8_step_list_kernel(const StepListArgs a) {
     __shared__ float2 tab[512];
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = xcd_block(blockIdx.x, gridDim.x) * (kBlock / 64) +
+    const int64_t chunk = xcd_eighth(blockIdx.x, gridDim.x) * (kBlock / 64) +
                           __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const bool live = chunk < a.total_chunks;
     int lo = 0;

@@ -5,8 +5,9 @@
 //
 // step_skeleton moves exactly the bytes of the step (14 + 32/G B per
 // parameter at G = 128) with the step's launch shape -- one 1024-parameter
-// chunk per wave, 256-thread workgroups in the same XCD-aware order, the same
-// residency cap -- and lane layout (16 consecutive parameters: 64 B of FP32
+// chunk per wave, 256-thread workgroups in the same XCD-aware order (each XCD
+// sweeping its own eighth of the launch), the same residency cap -- and lane
+// layout (16 consecutive parameters: 64 B of FP32
 // master weights, 32 B of BF16 gradient, 16 B of each FP8 moment, the group's
 // (amax, k) of both moments), with a trivial dependence on every loaded byte
 // in place of the arithmetic.  With meta = 0 it leaves out the per-group
@@ -29,12 +30,12 @@ struct SkelArgs {
 };
 
 // The step's XCD-aware workgroup order: the dispatcher deals workgroups to the
-// eight XCDs round-robin; each XCD sweeps runs of 256 consecutive logical
-// workgroups (blocks past the last whole run of 8 x 256 keep their index).
+// eight XCDs round-robin (workgroup b on XCD b % 8); XCD x sweeps logical
+// workgroups [x per, (x + 1) per) in order, per = nb / 8 (blocks past 8 per
+// keep their index).
 __device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t nb) {
-    if (b >= nb / 2048 * 2048) return b;
-    const int64_t q = b >> 3;
-    return (q / 256) * 2048 + (b & 7) * 256 + q % 256;
+    const int64_t per = nb >> 3;
+    return b < 8 * per ? (b & 7) * per + (b >> 3) : b;
 }
 
 template <bool kMeta>
