@@ -20,6 +20,10 @@ from the Infinity Cache).  The CPU baseline is the oracle on the host's
 cores: the 7B step on a contiguous 1/8 shard of the arena (extrapolated), and
 the other workloads in full.
 
+The step is also timed on a second copy of its buffers ("placement"): where
+the driver places them moves the step by several percent, and a process's
+first large allocation, which `value` measures, is usually a slow placement.
+
 Beside the step (not in `value`), "extras" times the other entry points on
 the same resident workloads: the step with its BF16 working copy, the step as a
 tensor-list launch (one entry per model tensor), the fused SwiGLU and RMSNorm
@@ -187,6 +191,26 @@ def state_diagnostics(st, sample=1 << 22):
                      "frac_k_below_1": round(float((k < 1).float().mean()), 5),
                      "frac_zero_groups": round(float((a == 0).float().mean()), 5)}
     return out
+
+
+def second_allocation_ms(coat, theta, grad, st, G, v_fmt, hp, step0, reps=5):
+    """The AdamW step timed again on a second copy of its buffers, allocated
+    while the first is still live (HIP events, `reps` launches after one
+    warm-up).  The step's time depends on where the driver places the
+    buffers, and a process's first large allocation is usually a slow
+    placement; the benchmark's value and roofline keep the first allocation,
+    this figure stands beside them."""
+    import torch
+
+    th2, g2 = theta.clone(), grad.clone()
+    s2 = {k: v.clone() for k, v in st.items()}
+    torch.cuda.synchronize()
+    ms = time_launches(lambda i: coat.coat_adamw_step(
+        th2, g2, s2["m_codes"], s2["m_amax"], s2["m_k"], s2["v_codes"], s2["v_amax"], s2["v_k"],
+        group_size=G, v_format=v_fmt, hp=hp(step0 + i)), reps)
+    del th2, g2, s2
+    torch.cuda.synchronize()
+    return ms
 
 
 def time_launches(fn, reps):
@@ -632,6 +656,10 @@ def main():
     achieved = alg["adamw_fp8_step"] / (per["adamw_fp8_step"] * 1e-3) / 1e9
     traffic = measured_traffic()
     diag = state_diagnostics(st)
+    log("the step on a second allocation of its buffers")
+    hp_at = lambda t: coat.adamw_hparams(f(inputs.LR), f(inputs.BETA1), f(inputs.BETA2), f(inputs.EPS),
+                                         f(inputs.WEIGHT_DECAY), t)
+    ms_second = second_allocation_ms(coat, theta, grad, st, G, spec.v_fmt, hp_at, step + 1)
     if not args.no_extras:
         log("extras: the other entry points and workloads")
     extra = None if args.no_extras else extras(coat, inputs, theta, grad, st, spec, G, step + 1)
@@ -677,6 +705,14 @@ def main():
             "device_ceiling": ceiling,
         },
         "cpu_baseline": cpu,
+        "placement": {
+            "first_allocation_adamw_ms": round(per["adamw_fp8_step"], 4),
+            "second_allocation_adamw_ms": round(ms_second, 4),
+            "second_allocation_frac_of_peak": round(alg["adamw_fp8_step"] / (ms_second * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": ("the same step on a second copy of its buffers, allocated while the first is live; "
+                     "the step's time depends on where the driver places the buffers, and value and "
+                     "roofline keep the first allocation"),
+        },
         "pages_context": {
             "note": ("figures the COAT explainer quotes for its own Hopper-class runs of OLMo training; "
                      "context, not targets, and not measured here"),
