@@ -21,8 +21,9 @@ cores: the 7B step on a contiguous 1/8 shard of the arena (extrapolated), and
 the other workloads in full.
 
 The step is also timed on a second copy of its buffers ("placement"): where
-the driver places them moves the step by several percent, and a process's
-first large allocation, which `value` measures, is usually a slow placement.
+the buffers land in device memory moves the step by several percent, and a
+process's first large allocation, which `value` measures, is usually a slow
+placement.
 
 Beside the step (not in `value`), "extras" times the other entry points on
 the same resident workloads: the step with its BF16 working copy, the step as a
@@ -196,8 +197,8 @@ def state_diagnostics(st, sample=1 << 22):
 def second_allocation_ms(coat, theta, grad, st, G, v_fmt, hp, step0, reps=5):
     """The AdamW step timed again on a second copy of its buffers, allocated
     while the first is still live (HIP events, `reps` launches after one
-    warm-up).  The step's time depends on where the driver places the
-    buffers, and a process's first large allocation is usually a slow
+    warm-up).  The step's time depends on where in device memory the
+    buffers land, and a process's first large allocation is usually a slow
     placement; the benchmark's value and roofline keep the first allocation,
     this figure stands beside them."""
     import torch
@@ -710,7 +711,7 @@ def main():
             "second_allocation_adamw_ms": round(ms_second, 4),
             "second_allocation_frac_of_peak": round(alg["adamw_fp8_step"] / (ms_second * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "note": ("the same step on a second copy of its buffers, allocated while the first is live; "
-                     "the step's time depends on where the driver places the buffers, and value and "
+                     "the step's time depends on where in device memory the buffers land, and value and "
                      "roofline keep the first allocation"),
         },
         "pages_context": {
